@@ -1,0 +1,17 @@
+"""Shared pytest set-up.
+
+Tests marked ``gpu`` need an MI355X (gfx950) and the built HIP library; all
+others run on the CPU.  The repository root is put on ``sys.path`` so that
+``oracle``, ``synth`` and ``int8_mqa_kv_amd`` import without installation.
+"""
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: takes more than a few seconds on the CPU")
