@@ -1,0 +1,231 @@
+/*
+ * mqa_kv.h -- C ABI of the int8 multi-query KV-cache attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes is defined by these pages:
+ *  - "Como funciona a inferência de IA, explicando claramente" (Red Hat),
+ *    section "Por que o cache KV existe": a new token's query is compared with
+ *    the key of every earlier token and the values are summed with those
+ *    weights; K and V are computed once per token and kept in GPU memory.
+ *    Section "Os modelos geram um token por vez": one new token per pass.
+ *  - same page, section "O que os servidores de inferência em produção ...
+ *    fazem a respeito?", item 1 (PagedAttention): the KV cache is cut into
+ *    small fixed-size blocks placed anywhere, with a per-request table that
+ *    says where each block is; item 3: prefix caching reuses cached K/V of a
+ *    shared opening.
+ *  - "Character.AI: inference optimization", section 03, technique table:
+ *    multi-query attention in all layers (one K/V head), local attention with
+ *    a horizon of 1024 interleaved with global layers (1 in 6 global), KV
+ *    shared across layers; section 05: int8 quantisation of the attention KV
+ *    cache; section 04: the KV of earlier turns is reused, so most turns
+ *    append a new message to a cached prefix.
+ *
+ * Readings where the pages are silent: the softmax scale defaults to
+ * 1/sqrt(head_dim); each token's K row and V row are coded as symmetric int8
+ * with one fp32 scale each, scale = max|x| / 127 and code = rint(x / scale)
+ * (ties to even) clamped to [-127, 127]; a window W covers the query's own
+ * position and the W-1 before it (W = 0: the whole history); a context length
+ * counts the current token (or appended chunk), whose K/V must already be
+ * packed.  Pages hold 16 tokens.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless marked (host).
+ *  - The caller owns every buffer (pool, tables, q, out, workspace).  The
+ *    library never allocates or frees on these paths and keeps no pointer
+ *    after it returns.
+ *  - Calls are asynchronous on `stream` (a hipStream_t passed as void*, NULL
+ *    for the null stream).  Buffers must stay alive until the stream passes
+ *    the call.  Calls on one stream are ordered; concurrent calls on
+ *    different streams must not share an output or workspace buffer.
+ *  - Every entry point returns an mqa_status.  Host-visible arguments are all
+ *    checked before anything is enqueued; on error nothing is enqueued or
+ *    written and mqa_last_error() describes the problem.  A launch failure
+ *    returns MQA_ERR_HIP.  Device-side contents (context lengths, page ids)
+ *    are clamped in the kernels so that bad values cannot read or write out
+ *    of bounds; they give undefined numbers instead.
+ */
+#ifndef MQA_KV_H
+#define MQA_KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MQA_KV_ABI_VERSION 1
+#define MQA_PAGE_TOKENS 16
+
+typedef enum {
+  MQA_OK = 0,
+  MQA_ERR_INVALID = -1,      /* a bad argument                                  */
+  MQA_ERR_UNSUPPORTED = -2,  /* a valid request this build does not implement   */
+  MQA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required      */
+  MQA_ERR_HIP = -4           /* the HIP runtime reported an error               */
+} mqa_status;
+
+typedef enum {
+  MQA_F32 = 0,               /* IEEE binary32                                   */
+  MQA_BF16 = 1               /* bfloat16 (upper half of a binary32)             */
+} mqa_dtype;
+
+/*
+ * The paged int8 KV pool.  One KV head per slot (multi-query attention).
+ * `base` points to `num_pages` page records of mqa_page_bytes(head_dim) bytes
+ * each, 256-byte aligned.  A page holds 16 consecutive tokens of one slot of
+ * one sequence: their int8 K codes, int8 V codes and fp32 K and V scales, all
+ * in one record so that one page read brings everything attention needs.
+ * Byte positions inside a record are given by mqa_page_offset(); the order is
+ * chosen so that each GPU lane's matrix-core operand is one contiguous
+ * 16-byte load.  Pages of every slot come from the same pool; which page
+ * holds which tokens is decided by the caller's block tables.
+ */
+typedef struct mqa_kv_pool {
+  void*   base;
+  int64_t num_pages;
+  int32_t head_dim;          /* 64 or 128                                       */
+  int32_t reserved;          /* must be 0                                       */
+} mqa_kv_pool;
+
+/* ABI version (MQA_KV_ABI_VERSION of the built library). */
+int mqa_abi_version(void);
+
+/* Text for the last non-OK status returned on this host thread ("" if none). */
+const char* mqa_last_error(void);
+
+/* Bytes of one page record: 32*head_dim + 128 (16 K rows, 16 V rows, 16+16
+ * fp32 scales).  0 for an unsupported head_dim. */
+size_t mqa_page_bytes(int32_t head_dim);
+
+/*
+ * Per-token KV bytes of a model, the formula of "Como funciona a inferência
+ * de IA", section "Qual é o tamanho real do cache KV?":
+ *   2 x num_layers x num_kv_heads x head_dim x dtype_bytes.
+ * For this library's cache (one KV head, int8 codes) add 8 bytes of fp32
+ * scales per token per slot.  Returns -1 for a negative argument.
+ */
+int64_t mqa_kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t dtype_bytes);
+
+/*
+ * Host-side layout query: byte offset inside a page record of token `token`
+ * (0..15), channel `channel` (0..head_dim-1) of K (`which` = 0) or V (1), or
+ * of that token's fp32 scale (`which` = 2 for K, 3 for V; `channel` ignored).
+ * Writes the offset to *offset (host) and returns MQA_OK, or MQA_ERR_INVALID.
+ */
+int mqa_page_offset(int32_t head_dim, int32_t token, int32_t channel,
+                    int32_t which, int64_t* offset);
+
+/*
+ * kv_pack_int8 -- quantise new tokens' K and V rows and write them into pages.
+ *
+ * Defined by: KV caching computes K and V once for each new token and keeps
+ * them (Red Hat page, "Por que o cache KV existe"); the cache is int8
+ * (Character.AI page, section 05) in fixed-size blocks found through a table
+ * (Red Hat page, PagedAttention).
+ *
+ *  k, v          [num_tokens rows] of head_dim values of `src_dtype`; row t
+ *                starts at element t*row_stride (row_stride >= head_dim).
+ *  slot_mapping  int64 [num_tokens]: page*16 + offset_in_page of each token;
+ *                a negative entry skips that token (padding).
+ *  pool          (host) the page pool written.
+ * For each token and each of K and V: a = max|x| over the row, s = a/127 in
+ * fp32, code = clamp(rint(x/s), -127, 127) with an IEEE fp32 division (all
+ * zeros when a = 0).  The result is bit-identical to that definition.
+ * Entries pointing outside the pool are skipped.  Two tokens mapped to the
+ * same position race; the caller must not do that.
+ */
+int kv_pack_int8(const void* k, const void* v, mqa_dtype src_dtype,
+                 int64_t num_tokens, int64_t row_stride,
+                 const int64_t* slot_mapping, const mqa_kv_pool* pool,
+                 void* stream);
+
+/*
+ * Workspace for mqa_decode_attn with the same shape arguments (the host
+ * arrays are read).  The workspace holds per-partition softmax partials of
+ * long contexts split across workgroups.  Returns 0 when none is needed or
+ * the arguments are invalid (a following mqa_decode_attn call reports why).
+ */
+size_t mqa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
+                                  int32_t num_layers, const int32_t* layer_slot,
+                                  const int32_t* layer_window,
+                                  int32_t max_context, int32_t head_dim);
+
+/*
+ * mqa_decode_attn -- one decode step of multi-query attention over the paged
+ * int8 cache: every query head of every listed layer of every sequence.
+ *
+ * Defined by: one new token per pass, whose query is compared with every
+ * cached key and whose output is the weighted sum of cached values (Red Hat
+ * page, "Os modelos geram um token por vez" and "Por que o cache KV existe");
+ * one shared K/V head per layer, local layers with a horizon, KV shared across
+ * layers (Character.AI page, section 03 table).
+ *
+ *  q             [num_layers][batch][num_q_heads][head_dim] of `q_dtype`.
+ *  out           fp32, same shape.  out = softmax(scale * q.khat^T) vhat over
+ *                the attended keys, khat = sK*codeK, vhat = sV*codeV.
+ *  block_table   int32 [num_slots][batch][max_pages_per_seq]: page ids in
+ *                the pool of the logical pages 0,1,2,... of each sequence in
+ *                each slot.  Entries for pages not attended are not read.
+ *  context_lens  int32 [batch]: cached tokens of each sequence including the
+ *                current one (which sits at position context_len-1).  Must
+ *                lie in [1, max_context]; a length <= 0 gives zeros.
+ *  max_context   (host) upper bound of context_lens, used to plan the launch
+ *                without reading device memory.
+ *  layer_slot    (host) int32 [num_layers]: the KV slot each layer reads.
+ *                Layers that read the same slot with the same window are
+ *                served from one KV read (cross-layer KV sharing).
+ *  layer_window  (host) int32 [num_layers]: 0 = global, W > 0 = the last W
+ *                positions (the query's own included).
+ *  softmax_scale <= 0 selects 1/sqrt(head_dim).
+ *  workspace     at least mqa_decode_workspace_bytes(...) bytes, 256-byte
+ *                aligned; contents need no initialisation.  May be NULL when
+ *                that size is 0.
+ * Supported: head_dim 64 or 128; q_dtype MQA_F32 or MQA_BF16; out fp32.
+ */
+int mqa_decode_attn(const void* q, mqa_dtype q_dtype, float* out,
+                    const mqa_kv_pool* pool, const int32_t* block_table,
+                    int32_t max_pages_per_seq, const int32_t* context_lens,
+                    int32_t max_context, int32_t batch, int32_t num_q_heads,
+                    int32_t num_layers, int32_t num_slots,
+                    const int32_t* layer_slot, const int32_t* layer_window,
+                    float softmax_scale, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
+ * mqa_append_attn -- causal attention of a multi-token chunk appended to a
+ * cached prefix (a new turn after a cross-turn cache hit, or prefill on top of
+ * a reused prefix).
+ *
+ * Defined by: the KV of earlier turns is kept and reused, so a new message is
+ * processed on top of the cached prefix (Character.AI page, section 04;
+ * Red Hat page, prefix caching); each token attends every earlier token and
+ * itself (Red Hat page, "Por que o cache KV existe"), limited by the layer's
+ * window (Character.AI page, section 03 table).
+ *
+ *  q             [num_layers][total_q][num_q_heads][head_dim] of `q_dtype`;
+ *                sequence b owns rows cu_q_lens[b] .. cu_q_lens[b+1]-1.
+ *  out           fp32, same shape.
+ *  context_lens  int32 [batch]: cached tokens including the whole chunk,
+ *                whose K/V must already be packed.  Token t of sequence b sits
+ *                at position context_lens[b] - q_len_b + t.
+ *  cu_q_lens     int32 [batch+1]: prefix sums of the chunk lengths
+ *                (cu_q_lens[0] = 0, cu_q_lens[batch] = total_q).
+ *  max_q_len     (host) upper bound of the chunk lengths.
+ * Other arguments as for mqa_decode_attn.  No workspace is needed.
+ */
+int mqa_append_attn(const void* q, mqa_dtype q_dtype, float* out,
+                    const mqa_kv_pool* pool, const int32_t* block_table,
+                    int32_t max_pages_per_seq, const int32_t* context_lens,
+                    const int32_t* cu_q_lens, int32_t max_context,
+                    int32_t max_q_len, int32_t total_q, int32_t batch,
+                    int32_t num_q_heads, int32_t num_layers, int32_t num_slots,
+                    const int32_t* layer_slot, const int32_t* layer_window,
+                    float softmax_scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MQA_KV_H */

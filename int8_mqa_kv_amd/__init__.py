@@ -1,0 +1,317 @@
+"""int8 multi-query KV-cache attention for AMD Instinct MI355X (gfx950).
+
+A thin Python binding over ``libmqa_kv.so`` (C ABI in ``include/mqa_kv.h``).
+Every step of the path runs in the library's HIP kernels; this module only
+turns torch tensors into pointers and sizes, and torch only provides device
+memory and streams.  The library must be built (``python -m
+int8_mqa_kv_amd.build``); importing fails loudly when it is not.
+
+Entry points (same names as the C ABI):
+  kv_pack_int8      quantise new K/V rows to int8 + fp32 scales into pages
+  mqa_decode_attn   one decode step over the paged int8 cache
+  mqa_append_attn   causal attention of an appended chunk on a cached prefix
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "PAGE_TOKENS", "MQAError", "KVPool", "lib", "page_bytes", "kv_bytes_per_token",
+    "page_layout", "kv_pack_int8", "decode_workspace_bytes", "mqa_decode_attn",
+    "mqa_append_attn", "slot_mapping_for", "unpack_page_tokens",
+]
+
+PAGE_TOKENS = 16
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmqa_kv.so")
+
+MQA_OK, MQA_ERR_INVALID, MQA_ERR_UNSUPPORTED, MQA_ERR_WORKSPACE, MQA_ERR_HIP = 0, -1, -2, -3, -4
+MQA_F32, MQA_BF16 = 0, 1
+
+
+class MQAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"status {status}: {message}")
+        self.status = status
+
+
+class _Pool(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("num_pages", ctypes.c_int64),
+                ("head_dim", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run `python -m int8_mqa_kv_amd.build` "
+                          "(hipcc, gfx950) before using the HIP path")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, i64, p, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    f32 = ctypes.c_float
+    L.mqa_abi_version.argtypes, L.mqa_abi_version.restype = [], ctypes.c_int
+    L.mqa_last_error.argtypes, L.mqa_last_error.restype = [], ctypes.c_char_p
+    L.mqa_page_bytes.argtypes, L.mqa_page_bytes.restype = [i32], sz
+    L.mqa_kv_bytes_per_token.argtypes, L.mqa_kv_bytes_per_token.restype = [i32, i32, i32, i32], i64
+    L.mqa_page_offset.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i64)]
+    L.mqa_page_offset.restype = ctypes.c_int
+    L.kv_pack_int8.argtypes = [p, p, ctypes.c_int, i64, i64, p, ctypes.POINTER(_Pool), p]
+    L.kv_pack_int8.restype = ctypes.c_int
+    L.mqa_decode_workspace_bytes.argtypes = [i32, i32, i32, p, p, i32, i32]
+    L.mqa_decode_workspace_bytes.restype = sz
+    L.mqa_decode_attn.argtypes = [p, ctypes.c_int, p, ctypes.POINTER(_Pool), p, i32, p, i32, i32,
+                                  i32, i32, i32, p, p, f32, p, sz, p]
+    L.mqa_decode_attn.restype = ctypes.c_int
+    L.mqa_append_attn.argtypes = [p, ctypes.c_int, p, ctypes.POINTER(_Pool), p, i32, p, p, i32,
+                                  i32, i32, i32, i32, i32, i32, p, p, f32, p]
+    L.mqa_append_attn.restype = ctypes.c_int
+    return L
+
+
+lib = _load()
+
+
+def _check(status: int) -> None:
+    if status != MQA_OK:
+        raise MQAError(status, lib.mqa_last_error().decode())
+
+
+def page_bytes(head_dim: int) -> int:
+    n = int(lib.mqa_page_bytes(head_dim))
+    if n == 0:
+        raise MQAError(MQA_ERR_UNSUPPORTED, f"head_dim {head_dim} unsupported")
+    return n
+
+
+def kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int, dtype_bytes: int) -> int:
+    return int(lib.mqa_kv_bytes_per_token(num_layers, num_kv_heads, head_dim, dtype_bytes))
+
+
+_layout_cache = {}
+
+
+def page_layout(head_dim: int):
+    """Byte offsets inside a page record, from the library's own layout:
+    ``(k_off [16, D], v_off [16, D], ks_off [16], vs_off [16])`` (int64)."""
+    if head_dim in _layout_cache:
+        return _layout_cache[head_dim]
+    off = ctypes.c_int64()
+    k = np.empty((PAGE_TOKENS, head_dim), np.int64)
+    v = np.empty((PAGE_TOKENS, head_dim), np.int64)
+    ks = np.empty(PAGE_TOKENS, np.int64)
+    vs = np.empty(PAGE_TOKENS, np.int64)
+    for j in range(PAGE_TOKENS):
+        for c in range(head_dim):
+            _check(lib.mqa_page_offset(head_dim, j, c, 0, ctypes.byref(off)))
+            k[j, c] = off.value
+            _check(lib.mqa_page_offset(head_dim, j, c, 1, ctypes.byref(off)))
+            v[j, c] = off.value
+        _check(lib.mqa_page_offset(head_dim, j, 0, 2, ctypes.byref(off)))
+        ks[j] = off.value
+        _check(lib.mqa_page_offset(head_dim, j, 0, 3, ctypes.byref(off)))
+        vs[j] = off.value
+    _layout_cache[head_dim] = (k, v, ks, vs)
+    return _layout_cache[head_dim]
+
+
+# --------------------------------------------------------------------------
+# torch plumbing
+# --------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev_ptr(t, name: str, dtype=None) -> int:
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _host_i32(x, n: int, name: str) -> np.ndarray:
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.int32).reshape(-1))
+    if a.size != n:
+        raise ValueError(f"{name} must have {n} entries")
+    return a
+
+
+class KVPool:
+    """A paged int8 KV pool in device memory (a torch uint8 tensor).
+
+    ``num_pages`` page records of ``page_bytes(head_dim)`` bytes.  Which
+    slot/sequence/tokens a page holds is decided by the caller's block tables.
+    """
+
+    def __init__(self, num_pages: int, head_dim: int, device="cuda", fill: Optional[int] = 0):
+        torch = _torch()
+        self.head_dim = int(head_dim)
+        self.num_pages = int(num_pages)
+        self.page_bytes = page_bytes(head_dim)
+        # torch's caching allocator returns 512-byte aligned blocks
+        if fill is None:
+            self.data = torch.empty((self.num_pages, self.page_bytes), dtype=torch.uint8,
+                                    device=device)
+        else:
+            self.data = torch.full((self.num_pages, self.page_bytes), fill, dtype=torch.uint8,
+                                   device=device)
+        self._c = _Pool(self.data.data_ptr(), self.num_pages, self.head_dim, 0)
+
+    @classmethod
+    def wrap(cls, data, head_dim: int) -> "KVPool":
+        """A pool over an existing uint8 tensor [num_pages, page_bytes]."""
+        obj = cls.__new__(cls)
+        obj.head_dim = int(head_dim)
+        obj.page_bytes = page_bytes(head_dim)
+        if data.dim() != 2 or data.shape[1] != obj.page_bytes:
+            raise ValueError("pool tensor must be [num_pages, page_bytes]")
+        obj.num_pages = int(data.shape[0])
+        obj.data = data
+        obj._c = _Pool(_dev_ptr(data, "pool"), obj.num_pages, obj.head_dim, 0)
+        return obj
+
+    @property
+    def c(self) -> _Pool:
+        return self._c
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return MQA_F32
+    if t.dtype == torch.bfloat16:
+        return MQA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+# --------------------------------------------------------------------------
+# Entry points
+# --------------------------------------------------------------------------
+def kv_pack_int8(k, v, slot_mapping, pool: KVPool, stream=None) -> None:
+    """Quantise K and V rows ``[T, head_dim]`` (fp32 or bf16, same dtype) and
+    write them at ``slot_mapping`` (int64 [T], page*16 + offset; negative =
+    skip)."""
+    torch = _torch()
+    if k.shape != v.shape or k.dtype != v.dtype:
+        raise ValueError("k and v must have the same shape and dtype")
+    if k.dim() != 2 or k.shape[1] != pool.head_dim:
+        raise ValueError("k and v must be [T, head_dim]")
+    t = int(k.shape[0])
+    if slot_mapping.shape != (t,):
+        raise ValueError("slot_mapping must be [T]")
+    _check(lib.kv_pack_int8(_dev_ptr(k, "k"), _dev_ptr(v, "v"), _dtype_code(k), t,
+                            pool.head_dim, _dev_ptr(slot_mapping, "slot_mapping", torch.int64),
+                            ctypes.byref(pool.c), _stream_ptr(stream)))
+
+
+def decode_workspace_bytes(batch: int, num_q_heads: int, layer_slot: Sequence[int],
+                           layer_window: Sequence[int], max_context: int, head_dim: int) -> int:
+    n = len(layer_slot)
+    ls = _host_i32(layer_slot, n, "layer_slot")
+    lw = _host_i32(layer_window, n, "layer_window")
+    return int(lib.mqa_decode_workspace_bytes(batch, num_q_heads, n, ls.ctypes.data,
+                                              lw.ctypes.data, max_context, head_dim))
+
+
+def mqa_decode_attn(q, out, pool: KVPool, block_table, context_lens, max_context: int,
+                    layer_slot: Sequence[int], layer_window: Sequence[int],
+                    softmax_scale: float = 0.0, workspace=None, stream=None) -> None:
+    """One decode step.  ``q [L, B, Hq, D]`` (fp32/bf16), ``out`` fp32 of the
+    same shape, ``block_table`` int32 [num_slots, B, max_pages],
+    ``context_lens`` int32 [B] (device), ``layer_slot``/``layer_window`` host
+    sequences of length L."""
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q must be [L, B, Hq, D]")
+    n_layers, batch, hq, d = (int(x) for x in q.shape)
+    if d != pool.head_dim:
+        raise ValueError("q head_dim does not match the pool")
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
+    if block_table.dim() != 3 or int(block_table.shape[1]) != batch:
+        raise ValueError("block_table must be [num_slots, B, max_pages]")
+    if tuple(context_lens.shape) != (batch,):
+        raise ValueError("context_lens must be [B]")
+    ls = _host_i32(layer_slot, n_layers, "layer_slot")
+    lw = _host_i32(layer_window, n_layers, "layer_window")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    _check(lib.mqa_decode_attn(
+        _dev_ptr(q, "q"), _dtype_code(q), _dev_ptr(out, "out", torch.float32), ctypes.byref(pool.c),
+        _dev_ptr(block_table, "block_table", torch.int32), int(block_table.shape[2]),
+        _dev_ptr(context_lens, "context_lens", torch.int32), int(max_context), batch, hq, n_layers,
+        int(block_table.shape[0]), ls.ctypes.data, lw.ctypes.data, float(softmax_scale), ws_ptr,
+        ws_bytes, _stream_ptr(stream)))
+
+
+def mqa_append_attn(q, out, pool: KVPool, block_table, context_lens, cu_q_lens, max_context: int,
+                    max_q_len: int, layer_slot: Sequence[int], layer_window: Sequence[int],
+                    softmax_scale: float = 0.0, stream=None) -> None:
+    """Causal chunk attention.  ``q [L, total_q, Hq, D]``; ``cu_q_lens`` int32
+    [B+1] (device); other arguments as for :func:`mqa_decode_attn`."""
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q must be [L, total_q, Hq, D]")
+    n_layers, total_q, hq, d = (int(x) for x in q.shape)
+    if d != pool.head_dim:
+        raise ValueError("q head_dim does not match the pool")
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
+    batch = int(context_lens.shape[0])
+    if block_table.dim() != 3 or int(block_table.shape[1]) != batch:
+        raise ValueError("block_table must be [num_slots, B, max_pages]")
+    if tuple(cu_q_lens.shape) != (batch + 1,):
+        raise ValueError("cu_q_lens must be [B+1]")
+    ls = _host_i32(layer_slot, n_layers, "layer_slot")
+    lw = _host_i32(layer_window, n_layers, "layer_window")
+    _check(lib.mqa_append_attn(
+        _dev_ptr(q, "q"), _dtype_code(q), _dev_ptr(out, "out", torch.float32), ctypes.byref(pool.c),
+        _dev_ptr(block_table, "block_table", torch.int32), int(block_table.shape[2]),
+        _dev_ptr(context_lens, "context_lens", torch.int32),
+        _dev_ptr(cu_q_lens, "cu_q_lens", torch.int32), int(max_context), int(max_q_len), total_q,
+        batch, hq, n_layers, int(block_table.shape[0]), ls.ctypes.data, lw.ctypes.data,
+        float(softmax_scale), _stream_ptr(stream)))
+
+
+# --------------------------------------------------------------------------
+# Host helpers (no device work)
+# --------------------------------------------------------------------------
+def slot_mapping_for(table_row: np.ndarray, start: int, stop: int) -> np.ndarray:
+    """page*16 + offset of positions [start, stop) of one sequence, given its
+    block-table row (logical page -> pool page)."""
+    pos = np.arange(start, stop, dtype=np.int64)
+    return np.asarray(table_row, dtype=np.int64)[pos // PAGE_TOKENS] * PAGE_TOKENS + pos % PAGE_TOKENS
+
+
+def unpack_page_tokens(pool_bytes: np.ndarray, slots: np.ndarray, head_dim: int):
+    """Read tokens back out of host copies of page records.
+
+    ``pool_bytes`` uint8 [num_pages, page_bytes]; ``slots`` int64 [T]
+    (page*16 + offset).  Returns ``(k_codes int8 [T, D], k_scales f32 [T],
+    v_codes int8 [T, D], v_scales f32 [T])``."""
+    k_off, v_off, ks_off, vs_off = page_layout(head_dim)
+    slots = np.asarray(slots, dtype=np.int64)
+    page, j = slots // PAGE_TOKENS, slots % PAGE_TOKENS
+    rec = pool_bytes[page]                                   # [T, page_bytes]
+    rows = np.arange(slots.size)[:, None]
+    kc = rec[rows, k_off[j]].view(np.int8)
+    vc = rec[rows, v_off[j]].view(np.int8)
+    ks = np.stack([rec[np.arange(slots.size), ks_off[j] + b] for b in range(4)], 1).copy()
+    vs = np.stack([rec[np.arange(slots.size), vs_off[j] + b] for b in range(4)], 1).copy()
+    return kc, ks.view(np.float32).reshape(-1), vc, vs.view(np.float32).reshape(-1)

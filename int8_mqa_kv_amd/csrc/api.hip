@@ -1,0 +1,382 @@
+// C entry points of libmqa_kv: argument checks, launch planning, launches.
+// Every check runs on the host before anything is enqueued.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "../../include/mqa_kv.h"
+#include "internal.hpp"
+
+using namespace mqa;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return MQA_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MQA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_pool(const mqa_kv_pool* pool) {
+  if (!pool) return fail(MQA_ERR_INVALID, "pool is NULL");
+  if (pool->head_dim != 64 && pool->head_dim != 128)
+    return fail(MQA_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", pool->head_dim);
+  if (pool->num_pages <= 0) return fail(MQA_ERR_INVALID, "pool has %lld pages",
+                                        (long long)pool->num_pages);
+  if (!pool->base) return fail(MQA_ERR_INVALID, "pool base is NULL");
+  if (!aligned(pool->base, 256)) return fail(MQA_ERR_INVALID, "pool base is not 256-byte aligned");
+  if (pool->reserved != 0) return fail(MQA_ERR_INVALID, "pool.reserved must be 0");
+  return MQA_OK;
+}
+
+// Shape checks common to decode and append.
+int check_attn_common(const void* q, mqa_dtype q_dtype, const float* out, const mqa_kv_pool* pool,
+                      const int32_t* block_table, int32_t max_pages_per_seq,
+                      const int32_t* context_lens, int32_t max_context, int32_t batch,
+                      int32_t num_q_heads, int32_t num_layers, int32_t num_slots,
+                      const int32_t* layer_slot, const int32_t* layer_window) {
+  int rc = check_pool(pool);
+  if (rc) return rc;
+  if (q_dtype != MQA_F32 && q_dtype != MQA_BF16)
+    return fail(MQA_ERR_UNSUPPORTED, "q dtype %d unsupported", (int)q_dtype);
+  if (batch <= 0) return fail(MQA_ERR_INVALID, "batch must be > 0 (got %d)", batch);
+  if (num_q_heads <= 0) return fail(MQA_ERR_INVALID, "num_q_heads must be > 0");
+  if (num_layers <= 0) return fail(MQA_ERR_INVALID, "num_layers must be > 0");
+  if (num_slots <= 0) return fail(MQA_ERR_INVALID, "num_slots must be > 0");
+  if (max_pages_per_seq <= 0) return fail(MQA_ERR_INVALID, "max_pages_per_seq must be > 0");
+  if (max_context <= 0) return fail(MQA_ERR_INVALID, "max_context must be > 0");
+  if ((int64_t)max_pages_per_seq * kPageTokens < max_context)
+    return fail(MQA_ERR_INVALID, "max_pages_per_seq*16 = %lld < max_context %d",
+                (long long)max_pages_per_seq * kPageTokens, max_context);
+  if (!q || !out || !block_table || !context_lens)
+    return fail(MQA_ERR_INVALID, "q, out, block_table and context_lens must be non-NULL");
+  if (!layer_slot || !layer_window)
+    return fail(MQA_ERR_INVALID, "layer_slot and layer_window (host arrays) must be non-NULL");
+  if (!aligned(q, 16) || !aligned(out, 16))
+    return fail(MQA_ERR_INVALID, "q and out must be 16-byte aligned");
+  if ((int64_t)num_slots * batch * max_pages_per_seq > INT64_C(1) << 40)
+    return fail(MQA_ERR_INVALID, "block table too large");
+  for (int l = 0; l < num_layers; ++l) {
+    if (layer_slot[l] < 0 || layer_slot[l] >= num_slots)
+      return fail(MQA_ERR_INVALID, "layer_slot[%d] = %d outside [0, %d)", l, layer_slot[l],
+                  num_slots);
+    if (layer_window[l] < 0)
+      return fail(MQA_ERR_INVALID, "layer_window[%d] = %d is negative", l, layer_window[l]);
+  }
+  return MQA_OK;
+}
+
+float scale_log2_of(float softmax_scale, int head_dim) {
+  const double s = softmax_scale > 0.0f ? (double)softmax_scale : 1.0 / sqrt((double)head_dim);
+  return (float)(s * 1.4426950408889634);
+}
+
+// ---------------------------------------------------------------------------
+// Decode planning
+// ---------------------------------------------------------------------------
+struct DecodePlan {
+  DecodeArgs args;
+  int nrt = 2;
+  size_t ws_bytes = 0;
+  bool need_merge = false;
+  int rc = MQA_OK;
+};
+
+// Workgroups the planner aims for: a few per compute unit of the 256, so that
+// every CU keeps several pages in flight.
+int target_workgroups() {
+  static const int v = [] {
+    const char* e = getenv("MQA_DECODE_TARGET_WGS");
+    const int t = e ? atoi(e) : 0;
+    return t > 0 ? t : 1024;
+  }();
+  return v;
+}
+
+int forced_pages_per_wave() {
+  static const int v = [] {
+    const char* e = getenv("MQA_DECODE_PAGES_PER_WAVE");
+    int t = e ? atoi(e) : 0;
+    if (t > 0 && (t & 1)) ++t;
+    return t;
+  }();
+  return v;
+}
+
+DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
+                       const int32_t* layer_slot, const int32_t* layer_window,
+                       int32_t max_context, int32_t head_dim) {
+  DecodePlan p;
+  DecodeArgs& a = p.args;
+  memset(&a, 0, sizeof a);
+  p.nrt = num_q_heads <= 16 ? 1 : 2;
+  const int head_blocks = (num_q_heads + kRowsPerBlock - 1) / kRowsPerBlock;
+
+  // groups of layers reading one slot with one window, in first-seen order
+  std::vector<std::pair<int, int>> keys;
+  std::vector<std::vector<int>> members;
+  for (int l = 0; l < num_layers; ++l) {
+    const std::pair<int, int> k{layer_slot[l], layer_window[l]};
+    auto it = std::find(keys.begin(), keys.end(), k);
+    if (it == keys.end()) {
+      keys.push_back(k);
+      members.push_back({l});
+    } else {
+      members[it - keys.begin()].push_back(l);
+    }
+  }
+  if ((int)keys.size() > kMaxGroups) {
+    p.rc = fail(MQA_ERR_UNSUPPORTED, "%d (slot, window) groups in one call; at most %d",
+                (int)keys.size(), kMaxGroups);
+    return p;
+  }
+  if (num_layers * head_blocks > kMaxRowBlocks) {
+    p.rc = fail(MQA_ERR_UNSUPPORTED, "%d row blocks (layers x ceil(heads/32)) in one call; at most %d",
+                num_layers * head_blocks, kMaxRowBlocks);
+    return p;
+  }
+
+  // pages a sequence can span in each group, and the total page work
+  std::vector<int64_t> max_np(keys.size());
+  int64_t total_pages = 0;
+  for (size_t g = 0; g < keys.size(); ++g) {
+    const int w = keys[g].second;
+    const int64_t span = w > 0 ? std::min<int64_t>(w, max_context) : max_context;
+    max_np[g] = (span + kPageTokens - 1) / kPageTokens + 1;
+    total_pages += max_np[g] * (int64_t)members[g].size() * head_blocks * batch;
+  }
+  int ppw = forced_pages_per_wave();
+  if (ppw <= 0) {
+    const double x = (double)total_pages / ((double)target_workgroups() * kAttnWaves);
+    ppw = std::max(2, 2 * (int)llround(x / 2.0));
+    ppw = std::min(ppw, 256);
+  }
+
+  int rb = 0;
+  int64_t wg = 0, ws = 0, merges = 0;
+  for (size_t g = 0; g < keys.size(); ++g) {
+    DecodeGroup& G = a.groups[g];
+    G.slot = keys[g].first;
+    G.window = keys[g].second;
+    G.first_rb = rb;
+    for (int l : members[g])
+      for (int hb = 0; hb < head_blocks; ++hb) {
+        a.rbs[rb].layer = l;
+        a.rbs[rb].head0 = hb * kRowsPerBlock;
+        a.rbs[rb].nrows = std::min(kRowsPerBlock, num_q_heads - hb * kRowsPerBlock);
+        ++rb;
+      }
+    G.num_rb = rb - G.first_rb;
+    G.pages_per_wave = ppw;
+    const int64_t ppc = (int64_t)ppw * kAttnWaves;
+    G.nchunk = (int)((max_np[g] + ppc - 1) / ppc);
+    G.wg_begin = (int)wg;
+    G.ws_begin = (int)ws;
+    wg += (int64_t)G.num_rb * batch * G.nchunk;
+    if (G.nchunk > 1) p.need_merge = true;
+    ws += (int64_t)G.num_rb * batch * G.nchunk;
+    merges += (int64_t)G.num_rb * batch;
+  }
+  if (wg > (INT64_C(1) << 30) || ws > (INT64_C(1) << 30)) {
+    p.rc = fail(MQA_ERR_UNSUPPORTED, "launch too large");
+    return p;
+  }
+  a.num_groups = (int)keys.size();
+  a.total_wgs = (int)wg;
+  a.total_merge = (int)merges;
+  p.ws_bytes = p.need_merge ? (size_t)ws * ws_record_floats(head_dim) * sizeof(float) : 0;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mqa_abi_version(void) { return MQA_KV_ABI_VERSION; }
+
+const char* mqa_last_error(void) { return g_last_error.c_str(); }
+
+size_t mqa_page_bytes(int32_t head_dim) {
+  return (head_dim == 64 || head_dim == 128) ? (size_t)page_bytes(head_dim) : 0;
+}
+
+int64_t mqa_kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t dtype_bytes) {
+  if (num_layers < 0 || num_kv_heads < 0 || head_dim < 0 || dtype_bytes < 0) return -1;
+  return INT64_C(2) * num_layers * num_kv_heads * head_dim * dtype_bytes;
+}
+
+int mqa_page_offset(int32_t head_dim, int32_t token, int32_t channel, int32_t which,
+                    int64_t* offset) {
+  if (head_dim != 64 && head_dim != 128)
+    return fail(MQA_ERR_UNSUPPORTED, "head_dim %d unsupported", head_dim);
+  if (token < 0 || token >= kPageTokens) return fail(MQA_ERR_INVALID, "token %d not in [0,16)", token);
+  if (!offset) return fail(MQA_ERR_INVALID, "offset is NULL");
+  if (which == 0 || which == 1) {
+    if (channel < 0 || channel >= head_dim)
+      return fail(MQA_ERR_INVALID, "channel %d not in [0,%d)", channel, head_dim);
+    *offset = which == 0 ? k_code_offset(head_dim, token, channel)
+                         : v_code_offset(head_dim, token, channel);
+  } else if (which == 2 || which == 3) {
+    *offset = which == 2 ? k_scale_offset(head_dim, token) : v_scale_offset(head_dim, token);
+  } else {
+    return fail(MQA_ERR_INVALID, "which = %d not in {0,1,2,3}", which);
+  }
+  return ok();
+}
+
+int kv_pack_int8(const void* k, const void* v, mqa_dtype src_dtype, int64_t num_tokens,
+                 int64_t row_stride, const int64_t* slot_mapping, const mqa_kv_pool* pool,
+                 void* stream) {
+  int rc = check_pool(pool);
+  if (rc) return rc;
+  if (src_dtype != MQA_F32 && src_dtype != MQA_BF16)
+    return fail(MQA_ERR_UNSUPPORTED, "source dtype %d unsupported", (int)src_dtype);
+  if (num_tokens < 0) return fail(MQA_ERR_INVALID, "num_tokens is negative");
+  if (num_tokens > (INT64_C(1) << 33)) return fail(MQA_ERR_INVALID, "num_tokens too large");
+  if (num_tokens == 0) return ok();
+  if (row_stride < pool->head_dim)
+    return fail(MQA_ERR_INVALID, "row_stride %lld < head_dim %d", (long long)row_stride,
+                pool->head_dim);
+  if (!k || !v || !slot_mapping) return fail(MQA_ERR_INVALID, "k, v and slot_mapping must be non-NULL");
+  const size_t esz = src_dtype == MQA_BF16 ? 2 : 4;
+  if (!aligned(k, esz) || !aligned(v, esz) || !aligned(slot_mapping, 8))
+    return fail(MQA_ERR_INVALID, "misaligned k, v or slot_mapping");
+  hipError_t e = launch_pack(pool->head_dim, src_dtype == MQA_BF16, k, v, num_tokens, row_stride,
+                             slot_mapping, static_cast<uint8_t*>(pool->base), pool->num_pages,
+                             static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "kv_pack_int8 launch");
+  return ok();
+}
+
+size_t mqa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_layers,
+                                  const int32_t* layer_slot, const int32_t* layer_window,
+                                  int32_t max_context, int32_t head_dim) {
+  if (batch <= 0 || num_q_heads <= 0 || num_layers <= 0 || max_context <= 0 || !layer_slot ||
+      !layer_window || (head_dim != 64 && head_dim != 128))
+    return 0;
+  for (int l = 0; l < num_layers; ++l)
+    if (layer_slot[l] < 0 || layer_window[l] < 0) return 0;
+  DecodePlan p = plan_decode(batch, num_q_heads, num_layers, layer_slot, layer_window,
+                             max_context, head_dim);
+  return p.rc ? 0 : p.ws_bytes;
+}
+
+int mqa_decode_attn(const void* q, mqa_dtype q_dtype, float* out, const mqa_kv_pool* pool,
+                    const int32_t* block_table, int32_t max_pages_per_seq,
+                    const int32_t* context_lens, int32_t max_context, int32_t batch,
+                    int32_t num_q_heads, int32_t num_layers, int32_t num_slots,
+                    const int32_t* layer_slot, const int32_t* layer_window, float softmax_scale,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_attn_common(q, q_dtype, out, pool, block_table, max_pages_per_seq, context_lens,
+                             max_context, batch, num_q_heads, num_layers, num_slots, layer_slot,
+                             layer_window);
+  if (rc) return rc;
+  DecodePlan p = plan_decode(batch, num_q_heads, num_layers, layer_slot, layer_window, max_context,
+                             pool->head_dim);
+  if (p.rc) return p.rc;
+  if (p.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < p.ws_bytes)
+      return fail(MQA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.ws_bytes,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 256)) return fail(MQA_ERR_INVALID, "workspace not 256-byte aligned");
+  }
+  DecodeArgs& a = p.args;
+  a.q = q;
+  a.out = out;
+  a.pool = static_cast<const uint8_t*>(pool->base);
+  a.num_pages = pool->num_pages;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.ws = static_cast<float*>(workspace);
+  a.max_pages = max_pages_per_seq;
+  a.max_context = max_context;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.scale_log2 = scale_log2_of(softmax_scale, pool->head_dim);
+  hipError_t e = launch_decode(pool->head_dim, q_dtype == MQA_F32, p.nrt, a, p.need_merge,
+                               static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mqa_decode_attn launch");
+  return ok();
+}
+
+int mqa_append_attn(const void* q, mqa_dtype q_dtype, float* out, const mqa_kv_pool* pool,
+                    const int32_t* block_table, int32_t max_pages_per_seq,
+                    const int32_t* context_lens, const int32_t* cu_q_lens, int32_t max_context,
+                    int32_t max_q_len, int32_t total_q, int32_t batch, int32_t num_q_heads,
+                    int32_t num_layers, int32_t num_slots, const int32_t* layer_slot,
+                    const int32_t* layer_window, float softmax_scale, void* stream) {
+  int rc = check_attn_common(q, q_dtype, out, pool, block_table, max_pages_per_seq, context_lens,
+                             max_context, batch, num_q_heads, num_layers, num_slots, layer_slot,
+                             layer_window);
+  if (rc) return rc;
+  if (!cu_q_lens) return fail(MQA_ERR_INVALID, "cu_q_lens must be non-NULL");
+  if (max_q_len <= 0) return fail(MQA_ERR_INVALID, "max_q_len must be > 0");
+  if (total_q <= 0) return fail(MQA_ERR_INVALID, "total_q must be > 0");
+  if (num_layers > kMaxLayers)
+    return fail(MQA_ERR_UNSUPPORTED, "%d layers in one append call; at most %d", num_layers,
+                kMaxLayers);
+  AppendArgs a;
+  memset(&a, 0, sizeof a);
+  const int head_blocks = (num_q_heads + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int token_blocks = (max_q_len + kAttnWaves - 1) / kAttnWaves;
+  const int64_t total = (int64_t)num_layers * batch * head_blocks * token_blocks;
+  if (total > (INT64_C(1) << 31) - 8) return fail(MQA_ERR_UNSUPPORTED, "launch too large");
+  // layers ordered by slot, so layers sharing a slot run back to back
+  std::vector<int> order(num_layers);
+  for (int l = 0; l < num_layers; ++l) order[l] = l;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int x, int y) { return layer_slot[x] < layer_slot[y]; });
+  for (int l = 0; l < num_layers; ++l) {
+    a.order[l] = order[l];
+    a.layer_slot[l] = layer_slot[l];
+    a.layer_window[l] = layer_window[l];
+  }
+  a.q = q;
+  a.out = out;
+  a.pool = static_cast<const uint8_t*>(pool->base);
+  a.num_pages = pool->num_pages;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.cu_q_lens = cu_q_lens;
+  a.max_pages = max_pages_per_seq;
+  a.max_context = max_context;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.total_q = total_q;
+  a.num_layers = num_layers;
+  a.head_blocks = head_blocks;
+  a.token_blocks = token_blocks;
+  a.total_wgs = (int)total;
+  a.scale_log2 = scale_log2_of(softmax_scale, pool->head_dim);
+  const int nrt = num_q_heads <= 16 ? 1 : 2;
+  hipError_t e = launch_append(pool->head_dim, q_dtype == MQA_F32, nrt, a,
+                               static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mqa_append_attn launch");
+  return ok();
+}
+
+}  // extern "C"

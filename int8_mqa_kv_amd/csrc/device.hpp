@@ -1,0 +1,81 @@
+// Device helpers shared by the gfx950 kernels: vector types, exact int8 ->
+// fp16 conversion, matrix-core wrapper, wavefront reductions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "layout.hpp"
+
+namespace mqa {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+template <typename T, typename F>
+__device__ __forceinline__ T bitcast(F f) {
+  static_assert(sizeof(T) == sizeof(F), "size");
+  return __builtin_bit_cast(T, f);
+}
+
+// Four int8 codes (one dword, byte k = code k) -> four exact fp16 values.
+// Bias each byte to u = code + 128 (xor 0x80), place it under the fp16
+// exponent of 1024 (bits 0x64uu = 1024 + u, exact for u < 1024) with one byte
+// permute per pair, then subtract 1152 = 1024 + 128 with a packed fp16 add.
+// Every step is exact: the results are the integers -127..127.
+__device__ __forceinline__ void i8x4_to_f16x4(uint32_t w, f16x2& lo, f16x2& hi) {
+  const uint32_t u = w ^ 0x80808080u;
+  // v_perm_b32: selector bytes 0-3 pick bytes of the second operand, 4-7 of
+  // the first.  Result bytes (low to high): u.b0, 0x64, u.b1, 0x64.
+  const uint32_t a = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+  const uint32_t b = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+  const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+  lo = bitcast<f16x2>(a) - bias;
+  hi = bitcast<f16x2>(b) - bias;
+}
+
+// Eight codes in two dwords -> one f16x8 operand (element k = byte k).
+__device__ __forceinline__ f16x8 i8x8_to_f16x8(uint32_t w0, uint32_t w1) {
+  f16x2 a, b, c, d;
+  i8x4_to_f16x4(w0, a, b);
+  i8x4_to_f16x4(w1, c, d);
+  return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// D = A.B + C on one 16x16x32 fp16 tile, fp32 accumulate.  Lane l
+// (i = l % 16, g = l / 16) supplies A[i][8g..8g+7] and B[8g..8g+7][i] and
+// receives D[4g..4g+3][i].
+__device__ __forceinline__ f32x4 mma16(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Reductions across the four lanes i, i+16, i+32, i+48 (one matrix row).
+__device__ __forceinline__ float row_max4(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+__device__ __forceinline__ float row_sum4(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Exponent E of x = m * 2^E with m in [0.5, 1) (x > 0, subnormals handled).
+__device__ __forceinline__ int frexp_exp(float x) { return __builtin_amdgcn_frexp_expf(x); }
+__device__ __forceinline__ float ldexp2(float x, int e) { return __builtin_amdgcn_ldexpf(x, e); }
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return bitcast<float>((uint32_t)b << 16);
+}
+
+}  // namespace mqa

@@ -1,0 +1,145 @@
+"""mqa_decode_attn on the GPU against the oracle (and GPU invariances).
+
+Tolerance: max |gpu - oracle| <= 2e-3 and ||gpu - oracle||_2 / ||oracle||_2 <=
+1e-3 over the whole output of each case.
+"""
+import numpy as np
+import pytest
+import torch
+
+import int8_mqa_kv_amd as mk
+import oracle
+import synth
+from tests.gpu_util import GpuCase, OracleKV, assert_parity, log, q_tensor
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_case(w, seqs=None):
+    log(f"decode case {w.case}: {w.name} B={w.batch} Hq={w.num_q_heads} d={w.head_dim} "
+        f"L={w.num_layers} q={w.q_dtype} maxctx={w.max_context}")
+    g = GpuCase(w)
+    q, q64 = q_tensor(w)
+    out = g.decode(q)
+    want = oracle.decode(q64, w.context_lens, w.layer_slot, w.layer_window, OracleKV(w),
+                         seqs=seqs)
+    got = out.cpu().numpy()
+    if seqs is not None:
+        got = got[:, seqs]
+    return g, q, out, assert_parity(got, want, f"case {w.case}")
+
+
+def test_case0_tiny_fp32_q():
+    _run_case(synth.case0())
+
+
+def test_case1_local_window_full_size():
+    _run_case(synth.case1())
+
+
+def test_case2_long_context_random_pages_outliers():
+    _run_case(synth.case2())
+
+
+def test_case3_three_layers_share_one_slot():
+    _run_case(synth.case3())
+
+
+EDGE = [
+    # (seed, batch, hq, d, q dtype, contexts, layers, window, permuted pool)
+    (1, 3, 8, 64, "f32", [1, 15, 16], 1, 0, 0),
+    (2, 4, 32, 128, "bf16", [17, 31, 32, 33], 1, 0, 64),
+    (3, 3, 32, 128, "bf16", [100, 1000, 2049], 1, 1, 0),
+    (4, 3, 32, 128, "bf16", [100, 1000, 2049], 1, 37, 300),
+    (5, 2, 32, 128, "bf16", [500, 3000], 1, 5000, 0),
+    (6, 5, 48, 128, "bf16", [1, 64, 65, 129, 700], 2, 0, 200),
+    (7, 2, 16, 64, "bf16", [33, 1234], 3, 100, 0),
+    (8, 2, 32, 128, "f32", [257, 4000], 1, 0, 400),
+    (9, 6, 32, 128, "bf16", [6000, 1, 7, 4096, 4097, 12345], 1, 1024, 3000),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[f"edge{c[0]}" for c in EDGE])
+def test_edge_shapes(case):
+    seed, batch, hq, d, qd, ctx, layers, window, perm = case
+    w = synth.custom_decode(seed, batch, hq, d, qd, ctx, layers, window, permuted_pool=perm)
+    _run_case(w)
+
+
+def test_mixed_windows_sharing_one_slot():
+    """Layers with different windows over one slot, plus a second slot."""
+    w = synth.custom_decode(20, 4, 32, 128, "bf16", [50, 1500, 3000, 2047], 4, 0,
+                            permuted_pool=1000)
+    g = GpuCase(w)
+    q, q64 = q_tensor(w)
+    ls, lw = [0, 0, 0, 0], [0, 1024, 1, 300]
+    out = g.decode(q, ls, lw)
+    want = oracle.decode(q64, w.context_lens, ls, lw, OracleKV(w))
+    assert_parity(out.cpu().numpy(), want, "mixed windows")
+
+
+def test_softmax_scale_argument():
+    w = synth.custom_decode(21, 2, 32, 128, "bf16", [300, 77], 1, 0)
+    g = GpuCase(w)
+    q, q64 = q_tensor(w)
+    out = g.decode(q, scale=0.05)
+    want = oracle.decode(q64, w.context_lens, w.layer_slot, w.layer_window, OracleKV(w),
+                         softmax_scale=0.05)
+    assert_parity(out.cpu().numpy(), want, "scale 0.05")
+
+
+def test_pages_outside_the_window_are_never_read():
+    """Overwrite every page before the window with NaN scales: bitwise the same."""
+    w = synth.case1()
+    g = GpuCase(w)
+    q, _ = q_tensor(w)
+    before = g.decode(q).clone()
+    _, _, ks_off, vs_off = mk.page_layout(w.head_dim)
+    nanb = torch.tensor(np.frombuffer(np.float32(np.nan).tobytes(), np.uint8).copy()).cuda()
+    pages = torch.from_numpy(w.block_table[0, :, :(4096 - 1024) // 16].reshape(-1).astype(np.int64)).cuda()
+    for j in range(16):
+        for b in range(4):
+            g.pool.data[pages, int(ks_off[j]) + b] = nanb[b]
+            g.pool.data[pages, int(vs_off[j]) + b] = nanb[b]
+    after = g.decode(q)
+    assert torch.equal(before, after)
+
+
+def test_page_permutation_invariance_and_determinism():
+    """The same logical cache through two different page placements gives
+    bitwise-equal output, and a rerun is bitwise equal."""
+    a = synth.custom_decode(30, 4, 32, 128, "bf16", [2000, 5000, 123, 4096], 1, 0,
+                            permuted_pool=1000)
+    b = synth.custom_decode(30, 4, 32, 128, "bf16", [2000, 5000, 123, 4096], 1, 0, permuted_pool=0)
+    b.seed_case = a.case  # same rows, different page placement
+    b.case = a.case
+    ga, gb = GpuCase(a), GpuCase(b)
+    assert not np.array_equal(a.block_table, b.block_table)
+    q, _ = q_tensor(a)
+    oa, ob, oa2 = ga.decode(q), gb.decode(q), ga.decode(q)
+    assert torch.equal(oa, ob)
+    assert torch.equal(oa, oa2)
+
+
+def test_shared_launch_equals_separate_launches():
+    w = synth.custom_decode(31, 4, 32, 128, "bf16", [3000, 100, 8000, 4500], 3, 0,
+                            permuted_pool=2000)
+    g = GpuCase(w)
+    q, q64 = q_tensor(w)
+    together = g.decode(q).cpu().numpy()
+    for li in range(3):
+        alone = g.decode(q[li:li + 1].contiguous(), [0], [0]).cpu().numpy()
+        np.testing.assert_allclose(together[li], alone[0], rtol=0, atol=2e-6)
+
+
+def test_output_only_written_where_expected():
+    """Canaries around the output stay intact."""
+    w = synth.custom_decode(32, 3, 32, 128, "bf16", [700, 2500, 9000], 1, 0)
+    g = GpuCase(w)
+    q, q64 = q_tensor(w)
+    big = torch.full((q.numel() + 2048,), 12345.0, dtype=torch.float32, device="cuda")
+    out = big[1024:1024 + q.numel()].view(tuple(q.shape))
+    g.decode(q, out=out)
+    assert torch.all(big[:1024] == 12345.0) and torch.all(big[-1024:] == 12345.0)
+    want = oracle.decode(q64, w.context_lens, w.layer_slot, w.layer_window, OracleKV(w))
+    assert_parity(out.cpu().numpy(), want, "canary case")
