@@ -1,0 +1,315 @@
+#!/usr/bin/env python3
+"""Throughput of the int8 MQA KV attention path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--case 1|2|3|4] [--gpus 1]
+
+One step is one pass of the whole hot path over one batch of synthetic input
+already resident in HBM:
+  decode cases (1-3): kv_pack_int8 of the current token of every sequence,
+                      then mqa_decode_attn over every layer of the case;
+  append case (4):    kv_pack_int8 of the appended chunk into every slot, then
+                      mqa_append_attn over all 12 layers.
+Inputs are rotated over replicas (pool, q, out, new rows) whose attended bytes
+together exceed 1 GB, so the 256 MB Infinity Cache and the L2s cannot serve a
+step from the previous one.  HIP events on the launch stream time the timed
+region and, inside it, every attention call.
+
+Prints one JSON line.  ``value`` is int8 KV GB/s of the whole step: the KV
+bytes the step must stream (codes + fp32 scales of every attended key of every
+slot, each once) divided by the step time.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak, published
+METRIC = "int8 KV GB/s (% of HBM peak) and decode tokens/s, MQA attention, 1 GPU"
+KERNEL_SOURCES = ["int8_mqa_kv_amd/csrc/attn.hip", "int8_mqa_kv_amd/csrc/device.hpp",
+                  "int8_mqa_kv_amd/csrc/internal.hpp", "int8_mqa_kv_amd/csrc/layout.hpp",
+                  "int8_mqa_kv_amd/csrc/api.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------------
+# Workload set-up on the GPU (all through the HIP path)
+# --------------------------------------------------------------------------
+class Replica:
+    pass
+
+
+def setup(w, replicas, torch, mk, synth):
+    dev = "cuda"
+    pool0 = mk.KVPool(w.num_pages, w.head_dim, device=dev)
+    bt = torch.from_numpy(np.ascontiguousarray(w.block_table)).to(dev)
+    ctx = torch.from_numpy(w.context_lens.astype(np.int32)).to(dev)
+    cu = torch.from_numpy(w.cu_q_lens.astype(np.int32)).to(dev)
+    # history of every slot, packed through kv_pack_int8
+    ks, vs, sm, n = [], [], [], 0
+
+    def flush():
+        nonlocal ks, vs, sm, n
+        if ks:
+            mk.kv_pack_int8(torch.from_numpy(np.concatenate(ks)).to(dev),
+                            torch.from_numpy(np.concatenate(vs)).to(dev),
+                            torch.from_numpy(np.concatenate(sm)).to(dev), pool0)
+            torch.cuda.synchronize()
+        ks, vs, sm, n = [], [], [], 0
+
+    for s in range(w.num_slots):
+        for b in range(w.batch):
+            first, c = w.stored_range(s, b)
+            k, v = w.kv_rows(s, b, first, c)
+            ks.append(k)
+            vs.append(v)
+            sm.append(mk.slot_mapping_for(w.block_table[s, b], first, c))
+            n += c - first
+            if n >= (1 << 20):
+                flush()
+    flush()
+    # the rows the step packs: the current token (decode) or the chunk (append)
+    nk, nv, nsm = [], [], []
+    for s in range(w.num_slots):
+        for b in range(w.batch):
+            c = int(w.context_lens[b])
+            first = c - int(w.q_lens[b])
+            k, v = w.kv_rows(s, b, first, c)
+            nk.append(k)
+            nv.append(v)
+            nsm.append(mk.slot_mapping_for(w.block_table[s, b], first, c))
+    new_k = torch.from_numpy(np.concatenate(nk)).to(dev)
+    new_v = torch.from_numpy(np.concatenate(nv)).to(dev)
+    new_sm = torch.from_numpy(np.concatenate(nsm)).to(dev)
+    qf = w.q_f32()
+    if w.q_dtype == "bf16":
+        q0 = torch.from_numpy(synth.f32_to_bf16_bits(qf).view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        q0 = torch.from_numpy(qf).to(dev)
+    reps = []
+    for r in range(replicas):
+        R = Replica()
+        if r == 0:
+            R.pool = pool0
+        else:
+            data = torch.empty_like(pool0.data)
+            data.copy_(pool0.data)
+            R.pool = mk.KVPool.wrap(data, w.head_dim)
+        R.q = q0 if r == 0 else q0.clone()
+        R.out = torch.empty(tuple(q0.shape), dtype=torch.float32, device=dev)
+        R.k = new_k if r == 0 else new_k.clone()
+        R.v = new_v if r == 0 else new_v.clone()
+        reps.append(R)
+    ws = None
+    if w.kind == "decode":
+        wsb = mk.decode_workspace_bytes(w.batch, w.num_q_heads, w.layer_slot, w.layer_window,
+                                        w.max_context, w.head_dim)
+        ws = torch.zeros(max(wsb, 256), dtype=torch.uint8, device=dev) if wsb else None
+    torch.cuda.synchronize()
+    return dict(bt=bt, ctx=ctx, cu=cu, sm=new_sm, reps=reps, ws=ws)
+
+
+def attn_call(w, st, R, mk):
+    if w.kind == "decode":
+        mk.mqa_decode_attn(R.q, R.out, R.pool, st["bt"], st["ctx"], w.max_context, w.layer_slot,
+                           w.layer_window, workspace=st["ws"])
+    else:
+        mk.mqa_append_attn(R.q, R.out, R.pool, st["bt"], st["ctx"], st["cu"], w.max_context,
+                           w.max_q_len, w.layer_slot, w.layer_window)
+
+
+def step(w, st, R, mk, ev=None):
+    mk.kv_pack_int8(R.k, R.v, st["sm"], R.pool)
+    if ev is not None:
+        ev[0].record()
+    attn_call(w, st, R, mk)
+    if ev is not None:
+        ev[1].record()
+
+
+def attention_flops(w) -> float:
+    """2*2*d flops per (query row, attended key): q.k and p*v."""
+    total = 0.0
+    for li in range(w.num_layers):
+        win = int(w.layer_window[li])
+        for b in range(w.batch):
+            c = int(w.context_lens[b])
+            ql = int(w.q_lens[b])
+            for t in range(ql):
+                p = c - ql + t
+                lo = max(0, p - win + 1) if win > 0 else 0
+                total += (p + 1 - lo)
+    return total * w.num_q_heads * 4 * w.head_dim
+
+
+# --------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the same step
+# --------------------------------------------------------------------------
+def cpu_baseline(w, kv_bytes_step, budget_s):
+    import oracle
+    qf = w.q_f32().astype(np.float64)
+    d = w.head_dim
+    # logical histories the oracle reads (set-up, untimed)
+    hist = {}
+    for s in range(w.num_slots):
+        for b in range(w.batch):
+            first, c = w.stored_range(s, b)
+            k, v = w.kv_rows(s, b, first, c)
+            hist[(s, b)] = (first, *oracle.quantize(k), *oracle.quantize(v))
+    new = [w.kv_rows(s, b, int(w.context_lens[b]) - int(w.q_lens[b]), int(w.context_lens[b]))
+           for s in range(w.num_slots) for b in range(w.batch)]
+    kv = lambda s, b: hist[(s, b)]
+    # sample: whole steps for the decode cases; for the append case a few
+    # sequences of one step (the unit is scaled by their share of the bytes)
+    seqs = list(range(w.batch))
+    frac = 1.0
+    if w.kind == "append":
+        seqs = list(range(0, w.batch, max(1, w.batch // 8)))[:8]
+        per = [sum(int(w.context_lens[b]) for _ in range(w.num_layers)) for b in range(w.batch)]
+        frac = sum(per[b] for b in seqs) / sum(per)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        for k, v in new:
+            oracle.quantize(k)
+            oracle.quantize(v)
+        if w.kind == "decode":
+            oracle.decode(qf, w.context_lens, w.layer_slot, w.layer_window, kv, seqs=seqs)
+        else:
+            oracle.append(qf, w.context_lens, w.cu_q_lens, w.layer_slot, w.layer_window, kv,
+                          seqs=seqs)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or (n >= 1 and el * (n + 1) / n > 3 * budget_s):
+            break
+    per_step = el / n / frac
+    sample = (f"{n} oracle step(s) of the same case" if w.kind == "decode" else
+              f"{n} pass(es) over {len(seqs)} of {w.batch} sequences, scaled to the whole step")
+    return {"value": kv_bytes_step / per_step / 1e9, "unit": "GB/s",
+            "cores": oracle.num_threads(), "kind": "oracle", "sample": sample,
+            "seconds": round(el, 3), "s_per_step": per_step,
+            "cpu": platform.processor() or platform.machine()}
+
+
+# --------------------------------------------------------------------------
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--case", type=int, default=1, choices=[1, 2, 3, 4])
+    ap.add_argument("--replicas", type=int, default=0, help="0: enough for >= 1 GB of KV")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}); the multi-GPU sharding is described in DESIGN.md, not run.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import int8_mqa_kv_amd as mk
+    import synth
+
+    w = synth.case(args.case)
+    kv_bytes = w.attended_keys() * (2 * w.head_dim + 8)
+    reps = args.replicas or max(1, math.ceil(1.0e9 / kv_bytes))
+    if w.kind == "append":
+        reps = args.replicas or 1   # footprint is several GB already
+    log(f"case {w.case}: {w.name}; KV bytes/step {kv_bytes}; replicas {reps}")
+    st = setup(w, reps, torch, mk, synth)
+    R = st["reps"]
+
+    for i in range(args.warmup):
+        step(w, st, R[i % reps], mk)
+    torch.cuda.synchronize()
+
+    E = torch.cuda.Event
+    evs = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(args.steps)]
+    t0, t1 = E(enable_timing=True), E(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(args.steps):
+        step(w, st, R[i % reps], mk, evs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms_step = total_ms / args.steps
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    log(f"step {ms_step * 1e3:.2f} us, attention call {attn_ms * 1e3:.2f} us")
+
+    tokens = int(w.q_lens.sum()) * w.num_layers
+    value = kv_bytes / (ms_step * 1e-3) / 1e9
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8 KV codes, fp16 matrix-core operands, fp32 accumulate",
+        "data": "synthetic (seeded)",
+        "config": {"workload": f"case {w.case}: {w.name}", "batch": w.batch,
+                   "num_q_heads": w.num_q_heads, "kv_heads": 1, "head_dim": w.head_dim,
+                   "layers": w.num_layers, "layer_window": w.layer_window.tolist(),
+                   "max_context": w.max_context, "q_dtype": w.q_dtype,
+                   "parallelism": "none (1 GPU)", "replicas": reps},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "decode_tokens_per_s" if w.kind == "decode" else "appended_tokens_per_s":
+            round(tokens / (ms_step * 1e-3), 1),
+        "kv_bytes_per_step": kv_bytes,
+    }
+    if w.kind == "decode":
+        achieved = kv_bytes / (attn_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        fl = attention_flops(w)
+        achieved = fl / (attn_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4)}
+    roof["kernel"] = "mqa_decode_attn" if w.kind == "decode" else "mqa_append_attn"
+    roof["avg_launch_us"] = round(attn_ms * 1e3, 3)
+    roof["traffic"] = traffic_from_profile(w.case, kv_bytes)
+    res["roofline"] = roof
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host cores ...")
+        res["cpu_baseline"] = cpu_baseline(w, kv_bytes, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def traffic_from_profile(case, kv_bytes):
+    """HBM bytes per attention call from the committed counter summary, when
+    it was taken on the current kernel sources (else null)."""
+    p = os.path.join(ROOT, "profiles", f"decode_counters_case{case}.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("traffic_bytes_per_call")
+
+
+if __name__ == "__main__":
+    main()

@@ -100,7 +100,8 @@ float scale_log2_of(float softmax_scale, int head_dim) {
 struct DecodePlan {
   DecodeArgs args;
   int nrt = 2;
-  size_t ws_bytes = 0;
+  size_t ws_bytes = 0;        // counters + partial records
+  size_t counter_bytes = 0;   // leading part of the workspace holding the counters
   bool need_merge = false;
   int rc = MQA_OK;
 };
@@ -111,7 +112,7 @@ int target_workgroups() {
   static const int v = [] {
     const char* e = getenv("MQA_DECODE_TARGET_WGS");
     const int t = e ? atoi(e) : 0;
-    return t > 0 ? t : 1024;
+    return t > 0 ? t : 512;
   }();
   return v;
 }
@@ -195,6 +196,7 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
     G.nchunk = (int)((max_np[g] + ppc - 1) / ppc);
     G.wg_begin = (int)wg;
     G.ws_begin = (int)ws;
+    G.merge_begin = (int)merges;
     wg += (int64_t)G.num_rb * batch * G.nchunk;
     if (G.nchunk > 1) p.need_merge = true;
     ws += (int64_t)G.num_rb * batch * G.nchunk;
@@ -207,7 +209,10 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
   a.num_groups = (int)keys.size();
   a.total_wgs = (int)wg;
   a.total_merge = (int)merges;
-  p.ws_bytes = p.need_merge ? (size_t)ws * ws_record_floats(head_dim) * sizeof(float) : 0;
+  if (p.need_merge) {
+    p.counter_bytes = ((size_t)merges * sizeof(uint32_t) + 255) / 256 * 256;
+    p.ws_bytes = p.counter_bytes + (size_t)ws * ws_record_floats(head_dim) * sizeof(float);
+  }
   return p;
 }
 
@@ -305,19 +310,22 @@ int mqa_decode_attn(const void* q, mqa_dtype q_dtype, float* out, const mqa_kv_p
     if (!aligned(workspace, 256)) return fail(MQA_ERR_INVALID, "workspace not 256-byte aligned");
   }
   DecodeArgs& a = p.args;
-  a.q = q;
-  a.out = out;
-  a.pool = static_cast<const uint8_t*>(pool->base);
   a.num_pages = pool->num_pages;
-  a.block_table = block_table;
-  a.context_lens = context_lens;
-  a.ws = static_cast<float*>(workspace);
   a.max_pages = max_pages_per_seq;
   a.max_context = max_context;
   a.batch = batch;
   a.num_q_heads = num_q_heads;
   a.scale_log2 = scale_log2_of(softmax_scale, pool->head_dim);
-  hipError_t e = launch_decode(pool->head_dim, q_dtype == MQA_F32, p.nrt, a, p.need_merge,
+  DecodePtrs ptrs;
+  ptrs.q = q;
+  ptrs.out = out;
+  ptrs.pool = static_cast<const uint8_t*>(pool->base);
+  ptrs.block_table = block_table;
+  ptrs.context_lens = context_lens;
+  ptrs.counters = static_cast<uint32_t*>(workspace);
+  ptrs.ws = p.ws_bytes ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + p.counter_bytes)
+                       : nullptr;
+  hipError_t e = launch_decode(pool->head_dim, q_dtype == MQA_F32, p.nrt, a, ptrs,
                                static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mqa_decode_attn launch");
   return ok();
@@ -355,13 +363,7 @@ int mqa_append_attn(const void* q, mqa_dtype q_dtype, float* out, const mqa_kv_p
     a.layer_slot[l] = layer_slot[l];
     a.layer_window[l] = layer_window[l];
   }
-  a.q = q;
-  a.out = out;
-  a.pool = static_cast<const uint8_t*>(pool->base);
   a.num_pages = pool->num_pages;
-  a.block_table = block_table;
-  a.context_lens = context_lens;
-  a.cu_q_lens = cu_q_lens;
   a.max_pages = max_pages_per_seq;
   a.max_context = max_context;
   a.batch = batch;
@@ -373,7 +375,14 @@ int mqa_append_attn(const void* q, mqa_dtype q_dtype, float* out, const mqa_kv_p
   a.total_wgs = (int)total;
   a.scale_log2 = scale_log2_of(softmax_scale, pool->head_dim);
   const int nrt = num_q_heads <= 16 ? 1 : 2;
-  hipError_t e = launch_append(pool->head_dim, q_dtype == MQA_F32, nrt, a,
+  AppendPtrs ptrs;
+  ptrs.q = q;
+  ptrs.out = out;
+  ptrs.pool = static_cast<const uint8_t*>(pool->base);
+  ptrs.block_table = block_table;
+  ptrs.context_lens = context_lens;
+  ptrs.cu_q_lens = cu_q_lens;
+  hipError_t e = launch_append(pool->head_dim, q_dtype == MQA_F32, nrt, a, ptrs,
                                static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mqa_append_attn launch");
   return ok();

@@ -84,40 +84,58 @@ struct QOps {
   float crow[NRT];  // 2^(E-15) * scale * log2(e): undoes the row's prescale
 };
 
-// Rows 16n + li of the block start at qrow0 + (16n + li) * D elements.
+// Raw query registers of one wavefront: rows 16n + li, channels lg*CH .. +CH.
 template <int D, int QS, int NRT>
-__device__ __forceinline__ void load_q(QOps<D, QS, NRT>& o, const void* qrow0, int nrows,
-                                       float scale_log2, int li, int lg) {
+struct QRaw {
+  static constexpr int N = (Geo<D>::CH * (QS == 1 ? 2 : 4)) / 16;  // 16-byte loads per row tile
+  u32x4 w[NRT][N];
+};
+
+// Issue the loads of the block's query rows (row r starts r*D elements after
+// qrow0).  Lanes of rows beyond nrows re-read the last row (convert_q zeroes
+// them), so that no load depends on a branch or a select.
+template <int D, int QS, int NRT>
+__device__ __forceinline__ void load_q_raw(QRaw<D, QS, NRT>& r, const void* __restrict__ qrow0,
+                                           int nrows, int li, int lg) {
+  constexpr int CH = Geo<D>::CH;
+  constexpr int esz = QS == 1 ? 2 : 4;
+#pragma unroll
+  for (int n = 0; n < NRT; ++n) {
+    const int row = min(16 * n + li, nrows - 1);
+    const uint8_t* p = static_cast<const uint8_t*>(qrow0) + ((int64_t)row * D + lg * CH) * esz;
+#pragma unroll
+    for (int i = 0; i < QRaw<D, QS, NRT>::N; ++i)
+      r.w[n][i] = *reinterpret_cast<const u32x4*>(p + 16 * i);
+  }
+}
+
+// Turn the raw rows into matrix-core operands: scale each row by a power of
+// two so that its largest |element| lies in [2^14, 2^15), then round to fp16
+// (exact for bf16 input; fp32 input becomes a sum of two fp16 terms).
+template <int D, int QS, int NRT>
+__device__ __forceinline__ void convert_q(QOps<D, QS, NRT>& o, const QRaw<D, QS, NRT>& r,
+                                          float scale_log2, int nrows, int li) {
   constexpr int CH = Geo<D>::CH;
 #pragma unroll
   for (int n = 0; n < NRT; ++n) {
-    const int r = 16 * n + li;
+    const bool live = 16 * n + li < nrows;
     float x[CH];
-    if (r < nrows) {
-      if constexpr (QS == 1) {  // bf16
-        const uint16_t* p = static_cast<const uint16_t*>(qrow0) + (int64_t)r * D + lg * CH;
+    if constexpr (QS == 1) {
 #pragma unroll
-        for (int c = 0; c < CH; c += 8) {
-          const u32x4 w = *reinterpret_cast<const u32x4*>(p + c);
+      for (int i = 0; i < QRaw<D, QS, NRT>::N; ++i)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x[c + 2 * e] = bitcast<float>(w[e] << 16);
-            x[c + 2 * e + 1] = bitcast<float>(w[e] & 0xffff0000u);
-          }
+        for (int e = 0; e < 4; ++e) {
+          x[8 * i + 2 * e] = bitcast<float>(r.w[n][i][e] << 16);
+          x[8 * i + 2 * e + 1] = bitcast<float>(r.w[n][i][e] & 0xffff0000u);
         }
-      } else {  // fp32
-        const float* p = static_cast<const float*>(qrow0) + (int64_t)r * D + lg * CH;
-#pragma unroll
-        for (int c = 0; c < CH; c += 4) {
-          const f32x4 w = *reinterpret_cast<const f32x4*>(p + c);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[c + e] = w[e];
-        }
-      }
     } else {
 #pragma unroll
-      for (int c = 0; c < CH; ++c) x[c] = 0.0f;
+      for (int i = 0; i < QRaw<D, QS, NRT>::N; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * i + e] = bitcast<float>(r.w[n][i][e]);
     }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) x[c] = live ? x[c] : 0.0f;
     float a = 0.0f;
 #pragma unroll
     for (int c = 0; c < CH; ++c) a = fmaxf(a, fabsf(x[c]));
@@ -257,46 +275,65 @@ __device__ __forceinline__ void attend_block(WaveState<D, NRT>& st, const QOps<D
   }
 }
 
-// Walk logical pages [pbeg, pend) of one (slot, sequence) two at a time, with
-// the next pair's loads issued before the current pair is computed.
-template <int D, int QS, int NRT>
-__device__ __forceinline__ void attend_pages(WaveState<D, NRT>& st, const QOps<D, QS, NRT>& q,
-                                             const uint8_t* pool, int64_t num_pages,
-                                             const int32_t* table_row, int pbeg, int pend,
-                                             int lo, int hi, int lane, int lg) {
-  if (pbeg >= pend) return;
+// Logical pages [pbeg, pend) of one (slot, sequence), read two at a time.
+// The wavefront keeps a window of 64 page ids in a register (lane i holds the
+// id of page wbase + i), filled by one coalesced load and handed out with
+// readlane, so the page loads never wait on a table read of their own.
+template <int D>
+struct PageStream {
+  const uint8_t* __restrict__ pool;
+  const int32_t* __restrict__ table_row;
+  int64_t num_pages;
+  int pend;
+  int lane, lg;
+  int ids, wbase;
   PageRegs<D> c0, c1;
   bool ok0, ok1;
-  auto fetch = [&](PageRegs<D>& r, int pi, bool& ok) {
-    ok = false;
-    if (pi < pend) {
-      const int pid = __builtin_amdgcn_readfirstlane(table_row[pi]);
-      ok = (uint32_t)pid < (uint64_t)num_pages;
-      if (ok) {
-        load_page<D>(r, pool + (int64_t)pid * page_bytes(D), lane, lg);
-        return;
-      }
+
+  __device__ __forceinline__ void load_ids(int from) {
+    wbase = from;
+    ids = from + lane < pend ? table_row[from + lane] : -1;
+  }
+  // Branch-free: a page outside [.., pend) or with an id outside the pool
+  // loads page 0 instead (it exists: num_pages >= 1) and is masked by ok.
+  template <bool RELOAD>
+  __device__ __forceinline__ void fetch(PageRegs<D>& r, int pi, bool& ok) {
+    if constexpr (RELOAD) {
+      if (pi - wbase >= 64) load_ids(pi);
     }
-    zero_page<D>(r);
-  };
-  fetch(c0, pbeg, ok0);
-  fetch(c1, pbeg + 1, ok1);
-  for (int pa = pbeg; pa < pend; pa += 2) {
+    const int pid = __builtin_amdgcn_readlane(ids, min(pi - wbase, 63));
+    ok = pi < pend && (uint32_t)pid < (uint64_t)num_pages;
+    load_page<D>(r, pool + (int64_t)(ok ? pid : 0) * page_bytes(D), lane, lg);
+  }
+  // issue the first pair's loads
+  template <bool RELOAD>
+  __device__ __forceinline__ void start(int pbeg) {
+    fetch<RELOAD>(c0, pbeg, ok0);
+    fetch<RELOAD>(c1, pbeg + 1, ok1);
+  }
+};
+
+// Attend pages [pbeg, ps.pend) whose first pair ps.start(pbeg) already issued;
+// the next pair's loads are issued before the current pair is computed.
+template <int D, int QS, int NRT, bool RELOAD>
+__device__ __forceinline__ void attend_pages(WaveState<D, NRT>& st, const QOps<D, QS, NRT>& q,
+                                             PageStream<D>& ps, int pbeg, int lo, int hi) {
+  for (int pa = pbeg; pa < ps.pend; pa += 2) {
     PageRegs<D> n0, n1;
     bool nok0 = false, nok1 = false;
-    const bool more = pa + 2 < pend;
+    const bool more = pa + 2 < ps.pend;
     if (more) {
-      fetch(n0, pa + 2, nok0);
-      fetch(n1, pa + 3, nok1);
+      ps.template fetch<RELOAD>(n0, pa + 2, nok0);
+      ps.template fetch<RELOAD>(n1, pa + 3, nok1);
     }
     const int pos0 = pa * kPageTokens;
-    const bool masked = !(ok0 && ok1 && pos0 >= lo && pos0 + 2 * kPageTokens <= hi);
-    attend_block<D, QS, NRT>(st, q, c0, c1, masked, ok0, ok1, pos0, lo, hi, lg);
+    const bool masked = !(ps.ok0 && ps.ok1 && pos0 >= lo && pos0 + 2 * kPageTokens <= hi);
+    attend_block<D, QS, NRT>(st, q, ps.c0, ps.c1, masked, ps.ok0, ps.ok1, pos0, lo, hi, ps.lg);
     if (more) {
-      c0 = n0;
-      c1 = n1;
-      ok0 = nok0;
-      ok1 = nok1;
+      ps.c0 = n0;
+      ps.c1 = n1;
+      ps.ok0 = nok0;
+      ps.ok1 = nok1;
     }
   }
 }
@@ -322,24 +359,81 @@ __device__ __forceinline__ int swizzled_block() {
 // ---------------------------------------------------------------------------
 // Decode: one workgroup = one (row block, sequence, chunk of pages)
 // ---------------------------------------------------------------------------
+struct DecodeWork {
+  DecodeGroup g;
+  RowBlock rb;
+  int rbl, seq, chunk;
+};
+
+__device__ __forceinline__ DecodeWork decode_work(const DecodeArgs& a, int w) {
+  int gi = 0;
+  while (gi + 1 < a.num_groups && w >= a.groups[gi + 1].wg_begin) ++gi;
+  DecodeWork d;
+  d.g = a.groups[gi];
+  int local = w - d.g.wg_begin;
+  d.rbl = local % d.g.num_rb;
+  local /= d.g.num_rb;
+  d.chunk = local % d.g.nchunk;
+  d.seq = local / d.g.nchunk;
+  d.rb = a.rbs[d.g.first_rb + d.rbl];
+  return d;
+}
+
+// Merge the nch partial records of one (row block, sequence) into the output.
+// 256 threads: thread t takes row t/8 and D/8 consecutive channels.
+template <int D>
+__device__ __forceinline__ void merge_records(const float* __restrict__ rec0, int nch, int nrows,
+                                              float* __restrict__ out_rows) {
+  const int row = threadIdx.x >> 3, part = threadIdx.x & 7;
+  if (row >= nrows) return;
+  constexpr int PER = D / 8;
+  constexpr int64_t RS = ws_record_floats(D);
+  float mm = kNegInf;
+  for (int c = 0; c < nch; ++c) mm = fmaxf(mm, rec0[c * RS + row]);
+  const float mu = mm == kNegInf ? 0.0f : mm;
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
+  float ll = 0.0f;
+  for (int c = 0; c < nch; ++c) {
+    const float* rec = rec0 + c * RS;
+    const float f = fast_exp2(rec[row] - mu);
+    ll += f * rec[32 + row];
+    const float* src = rec + 64 + row * D + part * PER;
+#pragma unroll
+    for (int e = 0; e < PER; e += 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(src + e);
+      acc[e] += f * x[0];
+      acc[e + 1] += f * x[1];
+      acc[e + 2] += f * x[2];
+      acc[e + 3] += f * x[3];
+    }
+  }
+  const float inv = ll > 0.0f ? 1.0f / ll : 0.0f;
+  float* o = out_rows + row * D + part * PER;
+#pragma unroll
+  for (int e = 0; e < PER; e += 4)
+    *reinterpret_cast<f32x4*>(o + e) =
+        f32x4{acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv};
+}
+
 template <int D, int QS, int NRT>
-__global__ __launch_bounds__(kAttnWaves * 64) void decode_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(kAttnWaves * 64) void decode_kernel(
+    const DecodeArgs a, const void* __restrict__ qp, float* __restrict__ out,
+    const uint8_t* __restrict__ pool, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ context_lens, float* __restrict__ ws,
+    uint32_t* __restrict__ counters) {
   constexpr int VT = Geo<D>::VT;
   const int w = swizzled_block();
   if (w >= a.total_wgs) return;
-  int gi = 0;
-  while (gi + 1 < a.num_groups && w >= a.groups[gi + 1].wg_begin) ++gi;
-  const DecodeGroup g = a.groups[gi];
-  int local = w - g.wg_begin;
-  const int rbl = local % g.num_rb;
-  local /= g.num_rb;
-  const int chunk = local % g.nchunk;
-  const int seq = local / g.nchunk;
-  const RowBlock rb = a.rbs[g.first_rb + rbl];
+  const DecodeWork dw = decode_work(a, w);
+  const DecodeGroup& g = dw.g;
+  const RowBlock& rb = dw.rb;
+  const int seq = dw.seq, chunk = dw.chunk;
 
   const int lane = lane_id(), li = lane & 15, lg = lane >> 4;
   const int wv = threadIdx.x >> 6;
-  const int ctx = clamp_ctx(a.context_lens[seq], a.max_context, a.max_pages);
+  const int ctx = clamp_ctx(context_lens[seq], a.max_context, a.max_pages);
   int lo, hi;
   decode_range(ctx, g.window, lo, hi);
   const int64_t out_row0 = ((int64_t)rb.layer * a.batch + seq) * a.num_q_heads + rb.head0;
@@ -350,7 +444,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void decode_kernel(const DecodeArg
         const int row = 16 * n + li;
         if (row < rb.nrows)
           for (int t = 0; t < VT; ++t)
-            *reinterpret_cast<f32x4*>(a.out + (out_row0 + row) * D + 16 * t + 4 * lg) =
+            *reinterpret_cast<f32x4*>(out + (out_row0 + row) * D + 16 * t + 4 * lg) =
                 f32x4{0, 0, 0, 0};
       }
     }
@@ -361,30 +455,46 @@ __global__ __launch_bounds__(kAttnWaves * 64) void decode_kernel(const DecodeArg
   const int nch = (p_last - p_first + ppc) / ppc;
   if (chunk >= nch) return;
 
+  // q loads first, then this wavefront's first page pair, then convert q
+  // while the pages are in flight.
+  // Order of the memory traffic: this wavefront's page ids, its query rows,
+  // its first page pair (once the ids are in); q is converted while the
+  // pages are in flight.
+  const int pbeg = p_first + chunk * ppc + wv * g.pages_per_wave;
+  PageStream<D> ps;
+  ps.pool = pool;
+  ps.table_row = block_table + ((int64_t)g.slot * a.batch + seq) * (int64_t)a.max_pages;
+  ps.num_pages = a.num_pages;
+  ps.pend = min(pbeg + g.pages_per_wave, p_last + 1);
+  ps.lane = lane;
+  ps.lg = lg;
+  ps.load_ids(pbeg);
+  constexpr int esz = QS == 1 ? 2 : 4;
+  QRaw<D, QS, NRT> qr;
+  load_q_raw<D, QS, NRT>(qr, static_cast<const uint8_t*>(qp) + out_row0 * D * esz, rb.nrows, li,
+                         lg);
+  ps.template start<false>(pbeg);  // branch-free: pages past pend load page 0, masked
+  // keep the page loads issued ahead of the q conversion
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
   QOps<D, QS, NRT> q;
-  const size_t esz = QS == 1 ? 2 : 4;
-  load_q<D, QS, NRT>(q, static_cast<const uint8_t*>(a.q) + out_row0 * D * esz, rb.nrows,
-                     a.scale_log2, li, lg);
+  convert_q<D, QS, NRT>(q, qr, a.scale_log2, rb.nrows, li);
 
   WaveState<D, NRT> st;
   st.init();
-  const int pbeg = p_first + chunk * ppc + wv * g.pages_per_wave;
-  const int pend = min(pbeg + g.pages_per_wave, p_last + 1);
-  const int32_t* table_row =
-      a.block_table + ((int64_t)g.slot * a.batch + seq) * (int64_t)a.max_pages;
-  attend_pages<D, QS, NRT>(st, q, a.pool, a.num_pages, table_row, pbeg, pend, lo, hi, lane, lg);
+  attend_pages<D, QS, NRT, false>(st, q, ps, pbeg, lo, hi);
 
   // ---- merge the wavefronts of the workgroup through LDS ----
   __shared__ float sm_m[kAttnWaves][32];
   __shared__ float sm_l[kAttnWaves][32];
   __shared__ f32x4 sm_acc[kAttnWaves - 1][NRT][VT][64];
-  float lrow[NRT];
+  __shared__ int sm_last;
 #pragma unroll
   for (int n = 0; n < NRT; ++n) {
-    lrow[n] = row_sum4(st.l[n]);
+    const float lrow = row_sum4(st.l[n]);
     if (lg == 0) {
       sm_m[wv][16 * n + li] = st.m[n];
-      sm_l[wv][16 * n + li] = lrow[n];
+      sm_l[wv][16 * n + li] = lrow;
     }
   }
   __syncthreads();
@@ -412,27 +522,36 @@ __global__ __launch_bounds__(kAttnWaves * 64) void decode_kernel(const DecodeArg
       for (int t = 0; t < VT; ++t) sm_acc[wv - 1][n][t][lane] = st.acc[n][t];
   }
   __syncthreads();
-  if (wv != 0) return;
+  if (wv == 0) {
 #pragma unroll
-  for (int x = 1; x < kAttnWaves; ++x)
+    for (int x = 1; x < kAttnWaves; ++x)
 #pragma unroll
-    for (int n = 0; n < NRT; ++n)
+      for (int n = 0; n < NRT; ++n)
 #pragma unroll
-      for (int t = 0; t < VT; ++t) st.acc[n][t] += sm_acc[x - 1][n][t][lane];
+        for (int t = 0; t < VT; ++t) st.acc[n][t] += sm_acc[x - 1][n][t][lane];
+  }
 
-  if (nch == 1) {
+  if (nch == 1) {  // the workgroup saw the whole range: write the output
+    if (wv != 0) return;
 #pragma unroll
     for (int n = 0; n < NRT; ++n) {
       const int row = 16 * n + li;
       if (row >= rb.nrows) continue;
       const float inv = L[n] > 0.0f ? 1.0f / L[n] : 0.0f;
-      float* o = a.out + (out_row0 + row) * D + 4 * lg;
+      float* o = out + (out_row0 + row) * D + 4 * lg;
 #pragma unroll
       for (int t = 0; t < VT; ++t) *reinterpret_cast<f32x4*>(o + 16 * t) = st.acc[n][t] * inv;
     }
-  } else {
-    float* rec = a.ws + ((int64_t)g.ws_begin + ((int64_t)rbl * a.batch + seq) * g.nchunk + chunk) *
-                            ws_record_floats(D);
+    return;
+  }
+
+  // ---- several chunks: publish this chunk's partial; the last chunk of the
+  // (row block, sequence) to arrive merges them all ----
+  const int64_t mi = (int64_t)g.merge_begin + (int64_t)dw.rbl * a.batch + seq;
+  float* rec0 =
+      ws + ((int64_t)g.ws_begin + ((int64_t)dw.rbl * a.batch + seq) * g.nchunk) * ws_record_floats(D);
+  if (wv == 0) {
+    float* rec = rec0 + (int64_t)chunk * ws_record_floats(D);
 #pragma unroll
     for (int n = 0; n < NRT; ++n) {
       const int row = 16 * n + li;
@@ -445,63 +564,17 @@ __global__ __launch_bounds__(kAttnWaves * 64) void decode_kernel(const DecodeArg
       for (int t = 0; t < VT; ++t) *reinterpret_cast<f32x4*>(o + 16 * t) = st.acc[n][t];
     }
   }
-}
-
-// ---------------------------------------------------------------------------
-// Decode merge: one workgroup = one (row block, sequence); 8 threads per row.
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
-  int w = blockIdx.x;
-  int gi = 0;
-  while (gi < a.num_groups && w >= a.groups[gi].num_rb * a.batch) {
-    w -= a.groups[gi].num_rb * a.batch;
-    ++gi;
+  __threadfence();  // release: the record is visible to every XCD before the count
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = atomicAdd(counters + mi, 1u);
+    sm_last = prev == (uint32_t)(nch - 1);
   }
-  if (gi >= a.num_groups) return;
-  const DecodeGroup g = a.groups[gi];
-  const int rbl = w / a.batch, seq = w % a.batch;
-  const RowBlock rb = a.rbs[g.first_rb + rbl];
-  const int ctx = clamp_ctx(a.context_lens[seq], a.max_context, a.max_pages);
-  int lo, hi;
-  decode_range(ctx, g.window, lo, hi);
-  if (hi <= lo) return;
-  const int ppc = g.pages_per_wave * kAttnWaves;
-  const int nch = ((hi - 1) / 16 - lo / 16 + ppc) / ppc;
-  if (nch <= 1) return;
-  const int row = threadIdx.x >> 3, part = threadIdx.x & 7;
-  if (row >= rb.nrows) return;
-  constexpr int PER = D / 8;
-  const float* rec0 = a.ws + ((int64_t)g.ws_begin + ((int64_t)rbl * a.batch + seq) * g.nchunk) *
-                                 ws_record_floats(D);
-  float mm = kNegInf;
-  for (int c = 0; c < nch; ++c) mm = fmaxf(mm, rec0[c * ws_record_floats(D) + row]);
-  const float mu = mm == kNegInf ? 0.0f : mm;
-  float acc[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
-  float ll = 0.0f;
-  for (int c = 0; c < nch; ++c) {
-    const float* rec = rec0 + c * ws_record_floats(D);
-    const float f = fast_exp2(rec[row] - mu);
-    ll += f * rec[32 + row];
-    const float* src = rec + 64 + row * D + part * PER;
-#pragma unroll
-    for (int e = 0; e < PER; e += 4) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(src + e);
-      acc[e] += f * x[0];
-      acc[e + 1] += f * x[1];
-      acc[e + 2] += f * x[2];
-      acc[e + 3] += f * x[3];
-    }
-  }
-  const float inv = ll > 0.0f ? 1.0f / ll : 0.0f;
-  float* o = a.out + (((int64_t)rb.layer * a.batch + seq) * a.num_q_heads + rb.head0 + row) * D +
-             part * PER;
-#pragma unroll
-  for (int e = 0; e < PER; e += 4)
-    *reinterpret_cast<f32x4*>(o + e) =
-        f32x4{acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv};
+  __syncthreads();
+  if (!sm_last) return;
+  __threadfence();  // acquire: see every other chunk's record
+  merge_records<D>(rec0, nch, rb.nrows, out + out_row0 * D);
+  if (threadIdx.x == 0) atomicExch(counters + mi, 0u);  // ready for the next call
 }
 
 // ---------------------------------------------------------------------------
@@ -510,7 +583,10 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
 // nearly coincide, so their page reads hit the same cache lines).
 // ---------------------------------------------------------------------------
 template <int D, int QS, int NRT>
-__global__ __launch_bounds__(kAttnWaves * 64) void append_kernel(const AppendArgs a) {
+__global__ __launch_bounds__(kAttnWaves * 64) void append_kernel(
+    const AppendArgs a, const void* __restrict__ qp, float* __restrict__ out,
+    const uint8_t* __restrict__ pool, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ cu_q_lens) {
   constexpr int VT = Geo<D>::VT;
   const int w = swizzled_block();
   if (w >= a.total_wgs) return;
@@ -529,11 +605,11 @@ __global__ __launch_bounds__(kAttnWaves * 64) void append_kernel(const AppendArg
 
   const int lane = lane_id(), li = lane & 15, lg = lane >> 4;
   const int wv = threadIdx.x >> 6;
-  const int q0 = a.cu_q_lens[seq];
-  const int qlen = a.cu_q_lens[seq + 1] - q0;
+  const int q0 = cu_q_lens[seq];
+  const int qlen = cu_q_lens[seq + 1] - q0;
   const int t = tb * kAttnWaves + wv;
   if (t >= qlen || q0 < 0 || q0 + t >= a.total_q) return;
-  const int ctx = clamp_ctx(a.context_lens[seq], a.max_context, a.max_pages);
+  const int ctx = clamp_ctx(context_lens[seq], a.max_context, a.max_pages);
   const int p = ctx - qlen + t;
   const int head0 = hb * kRowsPerBlock;
   const int nrows = min(kRowsPerBlock, a.num_q_heads - head0);
@@ -543,7 +619,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void append_kernel(const AppendArg
       const int row = 16 * n + li;
       if (row < nrows)
         for (int tt = 0; tt < VT; ++tt)
-          *reinterpret_cast<f32x4*>(a.out + (row0 + row) * D + 16 * tt + 4 * lg) =
+          *reinterpret_cast<f32x4*>(out + (row0 + row) * D + 16 * tt + 4 * lg) =
               f32x4{0, 0, 0, 0};
     }
     return;
@@ -551,22 +627,33 @@ __global__ __launch_bounds__(kAttnWaves * 64) void append_kernel(const AppendArg
   const int hi = p + 1;
   const int lo = window > 0 ? max(0, p - window + 1) : 0;
 
+  constexpr int esz = QS == 1 ? 2 : 4;
+  QRaw<D, QS, NRT> qr;
+  load_q_raw<D, QS, NRT>(qr, static_cast<const uint8_t*>(qp) + row0 * D * esz, nrows, li, lg);
+  const int pbeg = lo >> 4;
+  PageStream<D> ps;
+  ps.pool = pool;
+  ps.table_row = block_table + ((int64_t)slot * a.batch + seq) * (int64_t)a.max_pages;
+  ps.num_pages = a.num_pages;
+  ps.pend = ((hi - 1) >> 4) + 1;
+  ps.lane = lane;
+  ps.lg = lg;
+  ps.load_ids(pbeg);
+  ps.template start<true>(pbeg);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
   QOps<D, QS, NRT> q;
-  const size_t esz = QS == 1 ? 2 : 4;
-  load_q<D, QS, NRT>(q, static_cast<const uint8_t*>(a.q) + row0 * D * esz, nrows, a.scale_log2,
-                     li, lg);
+  convert_q<D, QS, NRT>(q, qr, a.scale_log2, nrows, li);
   WaveState<D, NRT> st;
   st.init();
-  const int32_t* table_row = a.block_table + ((int64_t)slot * a.batch + seq) * (int64_t)a.max_pages;
-  attend_pages<D, QS, NRT>(st, q, a.pool, a.num_pages, table_row, lo >> 4, ((hi - 1) >> 4) + 1, lo,
-                           hi, lane, lg);
+  attend_pages<D, QS, NRT, true>(st, q, ps, pbeg, lo, hi);
 #pragma unroll
   for (int n = 0; n < NRT; ++n) {
     const int row = 16 * n + li;
     const float l = row_sum4(st.l[n]);
     if (row >= nrows) continue;
     const float inv = (l > 0.0f && st.ev != kNoExp) ? ldexp2(1.0f / l, st.ev - 14) : 0.0f;
-    float* o = a.out + (row0 + row) * D + 4 * lg;
+    float* o = out + (row0 + row) * D + 4 * lg;
 #pragma unroll
     for (int tt = 0; tt < VT; ++tt) *reinterpret_cast<f32x4*>(o + 16 * tt) = st.acc[n][tt] * inv;
   }
@@ -578,18 +665,16 @@ __global__ __launch_bounds__(kAttnWaves * 64) void append_kernel(const AppendArg
 static inline dim3 padded_grid(int total) { return dim3((unsigned)((total + 7) / 8 * 8)); }
 
 template <int D, int QS, int NRT>
-static hipError_t launch_decode_t(const DecodeArgs& a, bool need_merge, hipStream_t stream) {
+static hipError_t launch_decode_t(const DecodeArgs& a, const DecodePtrs& p, hipStream_t stream) {
   hipLaunchKernelGGL((decode_kernel<D, QS, NRT>), padded_grid(a.total_wgs), dim3(kAttnWaves * 64),
-                     0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !need_merge) return e;
-  hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)a.total_merge), dim3(256), 0, stream, a);
+                     0, stream, a, p.q, p.out, p.pool, p.block_table, p.context_lens, p.ws,
+                     p.counters);
   return hipGetLastError();
 }
 
-hipError_t launch_decode(int D, bool q_f32, int nrt, const DecodeArgs& a, bool need_merge,
+hipError_t launch_decode(int D, bool q_f32, int nrt, const DecodeArgs& a, const DecodePtrs& p,
                          hipStream_t stream) {
-#define MQA_DEC(DD, QQ, NN) return launch_decode_t<DD, QQ, NN>(a, need_merge, stream)
+#define MQA_DEC(DD, QQ, NN) return launch_decode_t<DD, QQ, NN>(a, p, stream)
   if (D == 128) {
     if (q_f32) { if (nrt == 1) MQA_DEC(128, 2, 1); MQA_DEC(128, 2, 2); }
     if (nrt == 1) MQA_DEC(128, 1, 1);
@@ -602,14 +687,15 @@ hipError_t launch_decode(int D, bool q_f32, int nrt, const DecodeArgs& a, bool n
 }
 
 template <int D, int QS, int NRT>
-static hipError_t launch_append_t(const AppendArgs& a, hipStream_t stream) {
+static hipError_t launch_append_t(const AppendArgs& a, const AppendPtrs& p, hipStream_t stream) {
   hipLaunchKernelGGL((append_kernel<D, QS, NRT>), padded_grid(a.total_wgs), dim3(kAttnWaves * 64),
-                     0, stream, a);
+                     0, stream, a, p.q, p.out, p.pool, p.block_table, p.context_lens, p.cu_q_lens);
   return hipGetLastError();
 }
 
-hipError_t launch_append(int D, bool q_f32, int nrt, const AppendArgs& a, hipStream_t stream) {
-#define MQA_APP(DD, QQ, NN) return launch_append_t<DD, QQ, NN>(a, stream)
+hipError_t launch_append(int D, bool q_f32, int nrt, const AppendArgs& a, const AppendPtrs& p,
+                         hipStream_t stream) {
+#define MQA_APP(DD, QQ, NN) return launch_append_t<DD, QQ, NN>(a, p, stream)
   if (D == 128) {
     if (q_f32) { if (nrt == 1) MQA_APP(128, 2, 1); MQA_APP(128, 2, 2); }
     if (nrt == 1) MQA_APP(128, 1, 1);

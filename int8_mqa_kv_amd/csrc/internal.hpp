@@ -32,16 +32,12 @@ struct DecodeGroup {
   int32_t nchunk;          // chunks per sequence planned for max_context
   int32_t wg_begin;        // first flat workgroup of the group
   int32_t ws_begin;        // first workspace record of the group
+  int32_t merge_begin;     // first merge counter of the group (row blocks x batch before it)
+  int32_t pad;
 };
 
 struct DecodeArgs {
-  const void* q;
-  float* out;
-  const uint8_t* pool;
   int64_t num_pages;
-  const int32_t* block_table;
-  const int32_t* context_lens;
-  float* ws;
   int32_t max_pages;
   int32_t max_context;
   int32_t batch;
@@ -54,14 +50,20 @@ struct DecodeArgs {
   RowBlock rbs[kMaxRowBlocks];
 };
 
-struct AppendArgs {
+// Device buffers of a decode call (kernel parameters of their own, marked
+// __restrict__, so that uniform reads of tables become scalar loads).
+struct DecodePtrs {
   const void* q;
   float* out;
   const uint8_t* pool;
-  int64_t num_pages;
   const int32_t* block_table;
   const int32_t* context_lens;
-  const int32_t* cu_q_lens;
+  float* ws;            // partial records
+  uint32_t* counters;   // one arrival counter per (row block, sequence), zero between calls
+};
+
+struct AppendArgs {
+  int64_t num_pages;
   int32_t max_pages;
   int32_t max_context;
   int32_t batch;
@@ -78,14 +80,24 @@ struct AppendArgs {
   int32_t layer_window[kMaxLayers];
 };
 
+struct AppendPtrs {
+  const void* q;
+  float* out;
+  const uint8_t* pool;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  const int32_t* cu_q_lens;
+};
+
 hipError_t launch_pack(int D, bool bf16, const void* k, const void* v, int64_t num_tokens,
                        int64_t row_stride, const int64_t* slot_mapping, uint8_t* pool,
                        int64_t num_pages, hipStream_t stream);
 
-hipError_t launch_decode(int D, bool q_f32, int nrt, const DecodeArgs& a, bool need_merge,
+hipError_t launch_decode(int D, bool q_f32, int nrt, const DecodeArgs& a, const DecodePtrs& p,
                          hipStream_t stream);
 
-hipError_t launch_append(int D, bool q_f32, int nrt, const AppendArgs& a, hipStream_t stream);
+hipError_t launch_append(int D, bool q_f32, int nrt, const AppendArgs& a, const AppendPtrs& p,
+                         hipStream_t stream);
 
 // Decode workspace record: m[32], l[32], acc[32][D] fp32.
 constexpr int64_t ws_record_floats(int D) { return kRowsPerBlock * (D + 2); }

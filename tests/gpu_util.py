@@ -104,7 +104,13 @@ class GpuCase:
         if out is None:
             out = torch.full(tuple(q.shape), float("nan"), dtype=torch.float32, device=self.device)
         wsb = mk.decode_workspace_bytes(w.batch, w.num_q_heads, ls, lw, w.max_context, w.head_dim)
-        ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=self.device) if wsb else None
+        # The workspace is zeroed once and reused by every later call of this
+        # case (each call must leave its arrival counters at zero).
+        ws = None
+        if wsb:
+            if not hasattr(self, "_ws") or self._ws.numel() < wsb:
+                self._ws = torch.zeros(wsb, dtype=torch.uint8, device=self.device)
+            ws = self._ws
         mk.mqa_decode_attn(q, out, self.pool, self.block_table, self.context_lens, w.max_context,
                            ls, lw, softmax_scale=scale, workspace=ws)
         torch.cuda.synchronize()

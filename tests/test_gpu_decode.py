@@ -143,3 +143,17 @@ def test_output_only_written_where_expected():
     assert torch.all(big[:1024] == 12345.0) and torch.all(big[-1024:] == 12345.0)
     want = oracle.decode(q64, w.context_lens, w.layer_slot, w.layer_window, OracleKV(w))
     assert_parity(out.cpu().numpy(), want, "canary case")
+
+
+def test_workspace_reuse_across_calls():
+    """One zero-filled workspace serves many calls: the arrival counters are
+    back at zero after every call (case 2 splits every sequence)."""
+    w = synth.case2()
+    g = GpuCase(w)
+    q, q64 = q_tensor(w)
+    first = g.decode(q).clone()
+    ws_counters = g._ws[:4 * w.batch].clone()
+    assert torch.count_nonzero(ws_counters) == 0
+    for _ in range(3):
+        again = g.decode(q)
+        assert torch.equal(first, again)
