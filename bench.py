@@ -11,8 +11,12 @@ already resident in HBM:
                       mqa_append_attn over all 12 layers.
 Inputs are rotated over replicas (pool, q, out, new rows) whose attended bytes
 together exceed 1 GB, so the 256 MB Infinity Cache and the L2s cannot serve a
-step from the previous one.  HIP events on the launch stream time the timed
-region and, inside it, every attention call.
+step from the previous one.  By default the steps are replayed from HIP graphs
+(one step per replica per graph), as a serving loop replays its captured
+decode step; HIP events on the replay stream time the region.  The attention
+calls alone are timed the same way from a graph of only them: that average is
+the roofline's launch duration.  --no-graph launches every call from the host
+instead (then the host's launch rate, not the GPU, limits the small cases).
 
 Prints one JSON line.  ``value`` is int8 KV GB/s of the whole step: the KV
 bytes the step must stream (codes + fp32 scales of every attended key of every
@@ -209,6 +213,70 @@ def cpu_baseline(w, kv_bytes_step, budget_s):
             "cpu": platform.processor() or platform.machine()}
 
 
+def time_eager(w, st, R, reps, mk, torch, args):
+    """Host-launched steps; events around every attention call."""
+    for i in range(args.warmup):
+        step(w, st, R[i % reps], mk)
+    torch.cuda.synchronize()
+    E = torch.cuda.Event
+    evs = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(args.steps)]
+    t0, t1 = E(enable_timing=True), E(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(args.steps):
+        step(w, st, R[i % reps], mk, evs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / args.steps, float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def time_graphs(w, st, R, reps, mk, torch, args):
+    """Steps replayed from HIP graphs (one graph holds one step per replica),
+    as a serving loop replays its captured decode step.  The timed region is
+    exactly ``steps`` steps: full-graph replays plus one graph for the
+    remainder.  The attention calls alone are timed the same way from a graph
+    holding only them."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):          # warm up (and plan) outside capture
+        for i in range(max(args.warmup, 1)):
+            step(w, st, R[i % reps], mk)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+
+    def capture(fn, n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(i)
+        return g
+
+    full_n = min(reps, args.steps)
+    g_full = capture(lambda i: step(w, st, R[i], mk), full_n)
+    rem = args.steps % full_n
+    g_rem = capture(lambda i: step(w, st, R[i], mk), rem) if rem else None
+    a_full = capture(lambda i: attn_call(w, st, R[i], mk), full_n)
+    a_rem = capture(lambda i: attn_call(w, st, R[i], mk), rem) if rem else None
+    for g in (g_full, a_full):          # first replays are not timed
+        g.replay()
+    torch.cuda.synchronize()
+
+    def timed(gf, gr):
+        E = torch.cuda.Event
+        t0, t1 = E(enable_timing=True), E(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(args.steps // full_n):
+            gf.replay()
+        if gr is not None:
+            gr.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / args.steps
+
+    return timed(g_full, g_rem), timed(a_full, a_rem)
+
+
 # --------------------------------------------------------------------------
 def main():
     ap = argparse.ArgumentParser()
@@ -219,6 +287,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="0: enough for >= 1 GB of KV")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch every step from the host instead of replaying HIP graphs")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -241,22 +311,10 @@ def main():
     st = setup(w, reps, torch, mk, synth)
     R = st["reps"]
 
-    for i in range(args.warmup):
-        step(w, st, R[i % reps], mk)
-    torch.cuda.synchronize()
-
-    E = torch.cuda.Event
-    evs = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(args.steps)]
-    t0, t1 = E(enable_timing=True), E(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for i in range(args.steps):
-        step(w, st, R[i % reps], mk, evs[i])
-    t1.record()
-    torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
-    ms_step = total_ms / args.steps
-    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    if args.no_graph:
+        ms_step, attn_ms = time_eager(w, st, R, reps, mk, torch, args)
+    else:
+        ms_step, attn_ms = time_graphs(w, st, R, reps, mk, torch, args)
     log(f"step {ms_step * 1e3:.2f} us, attention call {attn_ms * 1e3:.2f} us")
 
     tokens = int(w.q_lens.sum()) * w.num_layers
@@ -288,6 +346,8 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4)}
     roof["kernel"] = "mqa_decode_attn" if w.kind == "decode" else "mqa_append_attn"
     roof["avg_launch_us"] = round(attn_ms * 1e3, 3)
+    roof["timing"] = ("host launches, events around each call" if args.no_graph else
+                      "HIP graph replay of back-to-back calls, events around the replays")
     roof["traffic"] = traffic_from_profile(w.case, kv_bytes)
     res["roofline"] = roof
     if not args.no_cpu_baseline:

@@ -143,11 +143,10 @@ int kv_pack_int8(const void* k, const void* v, mqa_dtype src_dtype,
 
 /*
  * Workspace for mqa_decode_attn with the same shape arguments (the host
- * arrays are read).  The workspace holds one arrival counter per (row block,
- * sequence) and the softmax partials of long contexts split across
- * workgroups; the last workgroup of a sequence to finish merges them.
- * Returns 0 when none is needed or the arguments are invalid (a following
- * mqa_decode_attn call reports why).
+ * arrays are read).  The workspace holds the softmax partials (max, sum,
+ * weighted values) of contexts split across workgroups; a second kernel of
+ * the same call merges them.  Returns 0 when none is needed or the arguments
+ * are invalid (a following mqa_decode_attn call reports why).
  */
 size_t mqa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                   int32_t num_layers, const int32_t* layer_slot,
@@ -182,11 +181,9 @@ size_t mqa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
  *                positions (the query's own included).
  *  softmax_scale <= 0 selects 1/sqrt(head_dim).
  *  workspace     at least mqa_decode_workspace_bytes(...) bytes, 256-byte
- *                aligned, ZERO-FILLED before its first use (it starts with
- *                the arrival counters of the chunks of each sequence; every
- *                call leaves them zero again, so one zero fill serves all
- *                later calls on the same stream).  May be NULL when that
- *                size is 0.  Calls sharing one workspace must not overlap.
+ *                aligned; contents need no initialisation.  May be NULL when
+ *                that size is 0.  Calls sharing one workspace must not
+ *                overlap (calls on one stream never do).
  * Supported: head_dim 64 or 128; q_dtype MQA_F32 or MQA_BF16; out fp32.
  */
 int mqa_decode_attn(const void* q, mqa_dtype q_dtype, float* out,

@@ -100,8 +100,8 @@ float scale_log2_of(float softmax_scale, int head_dim) {
 struct DecodePlan {
   DecodeArgs args;
   int nrt = 2;
-  size_t ws_bytes = 0;        // counters + partial records
-  size_t counter_bytes = 0;   // leading part of the workspace holding the counters
+  size_t ws_bytes = 0;        // partial records
+  int waves = 8;              // wavefronts per decode workgroup
   bool need_merge = false;
   int rc = MQA_OK;
 };
@@ -112,7 +112,16 @@ int target_workgroups() {
   static const int v = [] {
     const char* e = getenv("MQA_DECODE_TARGET_WGS");
     const int t = e ? atoi(e) : 0;
-    return t > 0 ? t : 512;
+    return t > 0 ? t : 384;
+  }();
+  return v;
+}
+
+int decode_waves() {
+  static const int v = [] {
+    const char* e = getenv("MQA_DECODE_WAVES");
+    const int t = e ? atoi(e) : 0;
+    return t == 8 ? 8 : 4;
   }();
   return v;
 }
@@ -169,11 +178,12 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
     max_np[g] = (span + kPageTokens - 1) / kPageTokens + 1;
     total_pages += max_np[g] * (int64_t)members[g].size() * head_blocks * batch;
   }
+  p.waves = decode_waves();
   int ppw = forced_pages_per_wave();
   if (ppw <= 0) {
-    const double x = (double)total_pages / ((double)target_workgroups() * kAttnWaves);
+    const double x = (double)total_pages / ((double)target_workgroups() * p.waves);
     ppw = std::max(2, 2 * (int)llround(x / 2.0));
-    ppw = std::min(ppw, 256);
+    ppw = std::min(ppw, 64);  // one register window of page ids per wavefront
   }
 
   int rb = 0;
@@ -192,7 +202,8 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
       }
     G.num_rb = rb - G.first_rb;
     G.pages_per_wave = ppw;
-    const int64_t ppc = (int64_t)ppw * kAttnWaves;
+    G.waves = p.waves;
+    const int64_t ppc = (int64_t)ppw * p.waves;
     G.nchunk = (int)((max_np[g] + ppc - 1) / ppc);
     G.wg_begin = (int)wg;
     G.ws_begin = (int)ws;
@@ -209,10 +220,7 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
   a.num_groups = (int)keys.size();
   a.total_wgs = (int)wg;
   a.total_merge = (int)merges;
-  if (p.need_merge) {
-    p.counter_bytes = ((size_t)merges * sizeof(uint32_t) + 255) / 256 * 256;
-    p.ws_bytes = p.counter_bytes + (size_t)ws * ws_record_floats(head_dim) * sizeof(float);
-  }
+  if (p.need_merge) p.ws_bytes = (size_t)ws * ws_record_floats(head_dim) * sizeof(float);
   return p;
 }
 
@@ -322,11 +330,9 @@ int mqa_decode_attn(const void* q, mqa_dtype q_dtype, float* out, const mqa_kv_p
   ptrs.pool = static_cast<const uint8_t*>(pool->base);
   ptrs.block_table = block_table;
   ptrs.context_lens = context_lens;
-  ptrs.counters = static_cast<uint32_t*>(workspace);
-  ptrs.ws = p.ws_bytes ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + p.counter_bytes)
-                       : nullptr;
-  hipError_t e = launch_decode(pool->head_dim, q_dtype == MQA_F32, p.nrt, a, ptrs,
-                               static_cast<hipStream_t>(stream));
+  ptrs.ws = p.ws_bytes ? static_cast<float*>(workspace) : nullptr;
+  hipError_t e = launch_decode(pool->head_dim, q_dtype == MQA_F32, p.nrt, p.waves, a, ptrs,
+                               p.need_merge, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mqa_decode_attn launch");
   return ok();
 }

@@ -178,14 +178,23 @@ struct WaveState {
   }
 };
 
+// Lazy softmax reference: a row's reference max only moves when a block's max
+// exceeds it by more than kTau (log2 units), so p = exp2(sigma - m_ref) stays
+// below 2^kTau and most blocks skip rescaling the accumulators.  P*sV is then
+// scaled by 2^(kPvBias - ev) (ev: exponent of the largest V scale seen), which
+// keeps the fp16 P operand below 2^14.
+constexpr float kTau = 8.0f;
+constexpr int kPvBias = 14 - 8;
+
 // Attend the 32 keys of two consecutive logical pages.  pos0 is the position
-// of the first page's first token; keys outside [lo, hi) or on a page that is
-// not ok are masked (their bytes are never used, so poison is harmless).
-template <int D, int QS, int NRT>
+// of the first page's first token.  MASKED blocks (some key outside [lo, hi)
+// or on a page that is not ok) select every masked key away, so poison bytes
+// in those keys are never used; interior blocks skip the selects.
+template <int D, int QS, int NRT, bool MASKED>
 __device__ __forceinline__ void attend_block(WaveState<D, NRT>& st, const QOps<D, QS, NRT>& q,
                                              const PageRegs<D>& p0, const PageRegs<D>& p1,
-                                             bool masked, bool ok0, bool ok1, int pos0, int lo,
-                                             int hi, int lg) {
+                                             bool ok0, bool ok1, int pos0, int lo, int hi,
+                                             int lg) {
   constexpr int KS = Geo<D>::KSTEPS;
   // S^T for both pages: lane (i, g) gets the scores of keys 4g..4g+3 for row i.
   f32x4 s[NRT][2];
@@ -211,7 +220,7 @@ __device__ __forceinline__ void attend_block(WaveState<D, NRT>& st, const QOps<D
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int pos = pos0 + 16 * u + 4 * lg + r;
-      valid[u][r] = !masked || ((u ? ok1 : ok0) && pos >= lo && pos < hi);
+      valid[u][r] = !MASKED || ((u ? ok1 : ok0) && pos >= lo && pos < hi);
     }
 
   // Largest valid V scale of the block -> running exponent (wave-uniform).
@@ -219,17 +228,21 @@ __device__ __forceinline__ void attend_block(WaveState<D, NRT>& st, const QOps<D
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (valid[u][r]) vmax = fmaxf(vmax, (u ? p1.sv : p0.sv)[r]);
+    for (int r = 0; r < 4; ++r) {
+      const float sv = (u ? p1.sv : p0.sv)[r];
+      vmax = fmaxf(vmax, MASKED ? (valid[u][r] ? sv : 0.0f) : sv);
+    }
   vmax = row_max4(vmax);
   int ev_new = st.ev;
-  // (clamped so that 2^(14-ev) stays finite for absurdly small scales)
+  // (clamped so that 2^(kPvBias-ev) stays finite for absurdly small scales)
   if (vmax > 0.0f) ev_new = max(ev_new, max(frexp_exp(vmax), -100));
   const int dexp = st.ev == kNoExp ? 0 : st.ev - ev_new;
   st.ev = ev_new;
-  const float pvm = ev_new == kNoExp ? 0.0f : ldexp2(1.0f, 14 - ev_new);
+  const float pvm = ev_new == kNoExp ? 0.0f : ldexp2(1.0f, kPvBias - ev_new);
 
   f16x8 pop[NRT];
+  float alpha[NRT];
+  bool rescale = false;
 #pragma unroll
   for (int n = 0; n < NRT; ++n) {
     float sig[2][4];
@@ -239,28 +252,38 @@ __device__ __forceinline__ void attend_block(WaveState<D, NRT>& st, const QOps<D
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float sk = (u ? p1.sk : p0.sk)[r];
-        sig[u][r] = valid[u][r] ? s[n][u][r] * (sk * q.crow[n]) : kNegInf;
+        const float x = s[n][u][r] * (sk * q.crow[n]);
+        sig[u][r] = MASKED ? (valid[u][r] ? x : kNegInf) : x;
         mx = fmaxf(mx, sig[u][r]);
       }
     mx = row_max4(mx);
-    const float m_new = fmaxf(st.m[n], mx);
+    const bool move = mx > st.m[n] + kTau;  // also true for the first valid block
+    const float m_new = move ? mx : st.m[n];
+    alpha[n] = move ? fast_exp2(st.m[n] - m_new) : 1.0f;  // exp2(-inf) = 0
+    rescale |= move;
     const float m_use = m_new == kNegInf ? 0.0f : m_new;
-    const float alpha = fast_exp2(st.m[n] - m_use);
     float ps = 0.0f;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = fast_exp2(sig[u][r] - m_use);
-        ps += p;
-        const float pv = valid[u][r] ? p * ((u ? p1.sv : p0.sv)[r] * pvm) : 0.0f;
-        pop[n][4 * u + r] = (_Float16)pv;
+        const float pr = fast_exp2(sig[u][r] - m_use);
+        ps += pr;
+        const float pv = pr * ((u ? p1.sv : p0.sv)[r] * pvm);
+        pop[n][4 * u + r] = (_Float16)(MASKED ? (valid[u][r] ? pv : 0.0f) : pv);
       }
-    st.l[n] = st.l[n] * alpha + ps;
+    st.l[n] = st.l[n] * alpha[n] + ps;
     st.m[n] = m_new;
-    const float ascale = ldexp2(alpha, dexp);
+  }
+  // rescale the accumulators only when some row's reference moved or the V
+  // exponent grew (wave-uniform branch)
+  if (__builtin_amdgcn_ballot_w64(rescale) != 0 || dexp != 0) {
 #pragma unroll
-    for (int t = 0; t < Geo<D>::VT; ++t) st.acc[n][t] *= ascale;
+    for (int n = 0; n < NRT; ++n) {
+      const float f = ldexp2(alpha[n], dexp);
+#pragma unroll
+      for (int t = 0; t < Geo<D>::VT; ++t) st.acc[n][t] *= f;
+    }
   }
 
 #pragma unroll
@@ -273,6 +296,18 @@ __device__ __forceinline__ void attend_block(WaveState<D, NRT>& st, const QOps<D
 #pragma unroll
     for (int n = 0; n < NRT; ++n) st.acc[n][t] = mma16(vop, pop[n], st.acc[n][t]);
   }
+}
+
+template <int D, int QS, int NRT>
+__device__ __forceinline__ void attend_block_any(WaveState<D, NRT>& st, const QOps<D, QS, NRT>& q,
+                                                 const PageRegs<D>& p0, const PageRegs<D>& p1,
+                                                 bool ok0, bool ok1, int pos0, int lo, int hi,
+                                                 int lg) {
+  const bool masked = !(ok0 && ok1 && pos0 >= lo && pos0 + 2 * kPageTokens <= hi);
+  if (masked)
+    attend_block<D, QS, NRT, true>(st, q, p0, p1, ok0, ok1, pos0, lo, hi, lg);
+  else
+    attend_block<D, QS, NRT, false>(st, q, p0, p1, ok0, ok1, pos0, lo, hi, lg);
 }
 
 // Logical pages [pbeg, pend) of one (slot, sequence), read two at a time.
@@ -326,9 +361,8 @@ __device__ __forceinline__ void attend_pages(WaveState<D, NRT>& st, const QOps<D
       ps.template fetch<RELOAD>(n0, pa + 2, nok0);
       ps.template fetch<RELOAD>(n1, pa + 3, nok1);
     }
-    const int pos0 = pa * kPageTokens;
-    const bool masked = !(ps.ok0 && ps.ok1 && pos0 >= lo && pos0 + 2 * kPageTokens <= hi);
-    attend_block<D, QS, NRT>(st, q, ps.c0, ps.c1, masked, ps.ok0, ps.ok1, pos0, lo, hi, ps.lg);
+    attend_block_any<D, QS, NRT>(st, q, ps.c0, ps.c1, ps.ok0, ps.ok1, pa * kPageTokens, lo, hi,
+                                 ps.lg);
     if (more) {
       ps.c0 = n0;
       ps.c1 = n1;
@@ -379,51 +413,166 @@ __device__ __forceinline__ DecodeWork decode_work(const DecodeArgs& a, int w) {
   return d;
 }
 
-// Merge the nch partial records of one (row block, sequence) into the output.
-// 256 threads: thread t takes row t/8 and D/8 consecutive channels.
+// ---------------------------------------------------------------------------
+// Page staging through LDS (gfx950 global -> LDS loads: lane l's 16 bytes land
+// at base + 16*l, which is exactly the page layout, so a page record moves
+// from HBM into LDS without passing through registers).
+// ---------------------------------------------------------------------------
+// LDS slot of one page: the record plus 128 bytes of padding that the
+// branch-free scale load below may write into.
 template <int D>
-__device__ __forceinline__ void merge_records(const float* __restrict__ rec0, int nch, int nrows,
-                                              float* __restrict__ out_rows) {
-  const int row = threadIdx.x >> 3, part = threadIdx.x & 7;
-  if (row >= nrows) return;
-  constexpr int PER = D / 8;
-  constexpr int64_t RS = ws_record_floats(D);
-  float mm = kNegInf;
-  for (int c = 0; c < nch; ++c) mm = fmaxf(mm, rec0[c * RS + row]);
-  const float mu = mm == kNegInf ? 0.0f : mm;
-  float acc[PER];
+constexpr int lds_slot_bytes() { return page_bytes(D) + 128; }
+
+template <int D>
+__device__ __forceinline__ void dma_page(uint8_t* lds_slot, const uint8_t* __restrict__ rec,
+                                         int lane) {
 #pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
-  float ll = 0.0f;
-  for (int c = 0; c < nch; ++c) {
-    const float* rec = rec0 + c * RS;
-    const float f = fast_exp2(rec[row] - mu);
-    ll += f * rec[32 + row];
-    const float* src = rec + 64 + row * D + part * PER;
-#pragma unroll
-    for (int e = 0; e < PER; e += 4) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(src + e);
-      acc[e] += f * x[0];
-      acc[e + 1] += f * x[1];
-      acc[e + 2] += f * x[2];
-      acc[e + 3] += f * x[3];
-    }
-  }
-  const float inv = ll > 0.0f ? 1.0f / ll : 0.0f;
-  float* o = out_rows + row * D + part * PER;
-#pragma unroll
-  for (int e = 0; e < PER; e += 4)
-    *reinterpret_cast<f32x4*>(o + e) =
-        f32x4{acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv};
+  for (int h = 0; h < 32 * D / 1024; ++h)
+    __builtin_amdgcn_global_load_lds(rec + h * 1024 + lane * 16, lds_slot + h * 1024, 16, 0, 0);
+  // the 128 bytes of fp32 scales: 4 bytes per lane; lanes 32..63 re-read the
+  // last scale and land in the slot's padding (no branch, no exec change)
+  __builtin_amdgcn_global_load_lds(rec + 32 * D + 4 * min(lane, 31), lds_slot + 32 * D, 4, 0, 0);
 }
 
-template <int D, int QS, int NRT>
-__global__ __launch_bounds__(kAttnWaves * 64) void decode_kernel(
+template <int D>
+__device__ __forceinline__ void lds_page(PageRegs<D>& r, const uint8_t* lds_slot, int lane,
+                                         int lg) {
+#pragma unroll
+  for (int h = 0; h < Geo<D>::KLOADS; ++h)
+    r.k[h] = *reinterpret_cast<const u32x4*>(lds_slot + h * 1024 + lane * 16);
+#pragma unroll
+  for (int h = 0; h < Geo<D>::VLOADS; ++h)
+    r.v[h] = *reinterpret_cast<const u32x4*>(lds_slot + 16 * D + h * 1024 + lane * 16);
+  r.sk = *reinterpret_cast<const f32x4*>(lds_slot + 32 * D + lg * 16);
+  r.sv = *reinterpret_cast<const f32x4*>(lds_slot + 32 * D + 64 + lg * 16);
+}
+
+// Decode workgroup LDS, as separate objects so that the compiler can tell the
+// page rings (written by global -> LDS loads) from everything else: q
+// operands converted once for all wavefronts, per-row softmax scales, the
+// wavefronts' softmax statistics, and each wavefront's 4-page ring, which the
+// final merge reuses once every page has been consumed.
+template <int D, int QS, int NRT, int W>
+struct DecodeQLds {
+  static constexpr int KS = Geo<D>::KSTEPS;
+  f16x8 q[NRT][QS][KS][64];
+  float crow[32];
+  float m[W][32];
+  float l[W][32];
+};
+template <int D, int NRT, int W>
+union DecodeRingLds {
+  static constexpr int RING = 4;
+  uint8_t ring[W][RING][lds_slot_bytes<D>()];
+  f32x4 acc[W / 2][NRT][Geo<D>::VT][64];
+};
+
+// The block's query rows staged into fp16 matrix-core operands in LDS, once
+// for all W wavefronts: wavefront w takes rows 4w..4w+3, 4w+4W.., 16 lanes per
+// row, D/16 channels per lane.  Loads first (StageQ::load), conversion later
+// (StageQ::store) so that other memory traffic can be issued in between.
+template <int D, int QS, int NRT, int W>
+struct StageQ {
+  static constexpr int PER = D / 16;                       // channels per lane
+  static constexpr int PASSES = (16 * NRT + 4 * W - 1) / (4 * W);
+  static constexpr int WORDS = PER * (QS == 1 ? 2 : 4) / 4;  // dwords per lane per pass
+  uint32_t raw[PASSES][WORDS];
+
+  __device__ __forceinline__ void load(const void* __restrict__ qrow0, int nrows, int wv,
+                                       int lane) {
+    constexpr int esz = QS == 1 ? 2 : 4;
+    const int sub = lane >> 4, part = lane & 15;
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int row = wv * 4 + ps * 4 * W + sub;
+      const int rr = row < nrows ? row : 0;
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(
+          static_cast<const uint8_t*>(qrow0) + ((int64_t)rr * D + part * PER) * esz);
+      if constexpr (WORDS == 4) {
+        const u32x4 w4 = *reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) raw[ps][e] = w4[e];
+      } else if constexpr (WORDS == 2) {
+        const u32x2 w2 = *reinterpret_cast<const u32x2*>(src);
+        raw[ps][0] = w2[0];
+        raw[ps][1] = w2[1];
+      } else {
+#pragma unroll
+        for (int e = 0; e < WORDS; e += 4) {
+          const u32x4 w4 = *reinterpret_cast<const u32x4*>(src + e);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) raw[ps][e + k] = w4[k];
+        }
+      }
+    }
+  }
+
+  template <typename Lds>
+  __device__ __forceinline__ void store(Lds& sm, int nrows, float scale_log2, int wv,
+                                        int lane) const {
+    constexpr int CH = Geo<D>::CH;
+    const int sub = lane >> 4, part = lane & 15;
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int row = min(wv * 4 + ps * 4 * W + sub, 16 * NRT - 1);
+      const bool live = row < nrows && wv * 4 + ps * 4 * W < 16 * NRT;
+      float x[PER];
+      if constexpr (QS == 1) {
+#pragma unroll
+        for (int e = 0; e < PER / 2; ++e) {
+          x[2 * e] = bitcast<float>(raw[ps][e] << 16);
+          x[2 * e + 1] = bitcast<float>(raw[ps][e] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) x[e] = bitcast<float>(raw[ps][e]);
+      }
+      float a = 0.0f;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        x[e] = live ? x[e] : 0.0f;
+        a = fmaxf(a, fabsf(x[e]));
+      }
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) a = fmaxf(a, __shfl_xor(a, off));
+      const int E = a > 0.0f ? max(frexp_exp(a), -100) : 15;
+      const float sc = ldexp2(1.0f, 15 - E);
+      if (part == 0) sm.crow[row] = ldexp2(scale_log2, E - 15);
+      // operand slot of (row, channels c0..c0+PER-1): tile n, lane (li, lg), step ks
+      const int c0 = part * PER;
+      const int n = row >> 4, li = row & 15;
+      const int lg = c0 / CH, ks = (c0 % CH) >> 3, e0 = c0 & 7;
+      _Float16 h1[PER], h2[PER];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const float y = x[e] * sc;
+        h1[e] = (_Float16)y;
+        h2[e] = (_Float16)(y - (float)h1[e]);
+      }
+#pragma unroll
+      for (int qs = 0; qs < QS; ++qs) {
+        const _Float16* h = qs == 0 ? h1 : h2;
+        if constexpr (PER == 8) {
+          sm.q[n][qs][ks][16 * lg + li] = f16x8{h[0], h[1], h[2], h[3], h[4], h[5], h[6], h[7]};
+        } else {
+          _Float16* d = reinterpret_cast<_Float16*>(&sm.q[n][qs][ks][16 * lg + li]) + e0;
+#pragma unroll
+          for (int e = 0; e < PER; ++e) d[e] = h[e];
+        }
+      }
+    }
+  }
+};
+
+template <int D, int QS, int NRT, int W>
+__global__ __launch_bounds__(W * 64) void decode_kernel(
     const DecodeArgs a, const void* __restrict__ qp, float* __restrict__ out,
     const uint8_t* __restrict__ pool, const int32_t* __restrict__ block_table,
-    const int32_t* __restrict__ context_lens, float* __restrict__ ws,
-    uint32_t* __restrict__ counters) {
+    const int32_t* __restrict__ context_lens, float* __restrict__ ws) {
   constexpr int VT = Geo<D>::VT;
+  constexpr int KS = Geo<D>::KSTEPS;
+  __shared__ DecodeQLds<D, QS, NRT, W> sm;
+  __shared__ DecodeRingLds<D, NRT, W> ring;
   const int w = swizzled_block();
   if (w >= a.total_wgs) return;
   const DecodeWork dw = decode_work(a, w);
@@ -451,88 +600,117 @@ __global__ __launch_bounds__(kAttnWaves * 64) void decode_kernel(
     return;
   }
   const int p_first = lo >> 4, p_last = (hi - 1) >> 4;
-  const int ppc = g.pages_per_wave * kAttnWaves;
+  const int ppc = g.pages_per_wave * W;
   const int nch = (p_last - p_first + ppc) / ppc;
   if (chunk >= nch) return;
 
-  // q loads first, then this wavefront's first page pair, then convert q
+  // Memory traffic in this order: the query rows and this wavefront's page
+  // ids together, then the first page pair straight into LDS; q is converted
   // while the pages are in flight.
-  // Order of the memory traffic: this wavefront's page ids, its query rows,
-  // its first page pair (once the ids are in); q is converted while the
-  // pages are in flight.
+  StageQ<D, QS, NRT, W> sq;
+  sq.load(static_cast<const uint8_t*>(qp) + out_row0 * D * (QS == 1 ? 2 : 4), rb.nrows, wv, lane);
   const int pbeg = p_first + chunk * ppc + wv * g.pages_per_wave;
-  PageStream<D> ps;
-  ps.pool = pool;
-  ps.table_row = block_table + ((int64_t)g.slot * a.batch + seq) * (int64_t)a.max_pages;
-  ps.num_pages = a.num_pages;
-  ps.pend = min(pbeg + g.pages_per_wave, p_last + 1);
-  ps.lane = lane;
-  ps.lg = lg;
-  ps.load_ids(pbeg);
-  constexpr int esz = QS == 1 ? 2 : 4;
-  QRaw<D, QS, NRT> qr;
-  load_q_raw<D, QS, NRT>(qr, static_cast<const uint8_t*>(qp) + out_row0 * D * esz, rb.nrows, li,
-                         lg);
-  ps.template start<false>(pbeg);  // branch-free: pages past pend load page 0, masked
-  // keep the page loads issued ahead of the q conversion
-  asm volatile("" ::: "memory");
+  const int pend = min(pbeg + g.pages_per_wave, p_last + 1);
+  const int32_t* table_row = block_table + ((int64_t)g.slot * a.batch + seq) * (int64_t)a.max_pages;
+  const int ids = pbeg + lane < pend ? table_row[pbeg + lane] : -1;
+  auto page_ok = [&](int pi, int& pid) {
+    pid = __builtin_amdgcn_readlane(ids, min(max(pi - pbeg, 0), 63));
+    return pi < pend && (uint32_t)pid < (uint64_t)a.num_pages;
+  };
+  // branch-free: a page that is out of range or has a bad id loads page 0
+  // instead (it exists) and is masked later
+  auto issue_block = [&](int pa, int slot0) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      int pid;
+      const bool ok = page_ok(pa + u, pid);
+      dma_page<D>(ring.ring[wv][slot0 + u], pool + (int64_t)(ok ? pid : 0) * page_bytes(D), lane);
+    }
+  };
+  const int nblk = (pend - pbeg + 1) >> 1;
+  issue_block(pbeg, 0);  // unconditional (a wave without pages loads page 0, unused)
   __builtin_amdgcn_sched_barrier(0);
+  sq.store(sm, rb.nrows, a.scale_log2, wv, lane);
+  __syncthreads();
   QOps<D, QS, NRT> q;
-  convert_q<D, QS, NRT>(q, qr, a.scale_log2, rb.nrows, li);
+#pragma unroll
+  for (int n = 0; n < NRT; ++n) {
+    q.crow[n] = sm.crow[16 * n + li];
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) q.q[n][qs][ks] = sm.q[n][qs][ks][lane];
+  }
 
   WaveState<D, NRT> st;
   st.init();
-  attend_pages<D, QS, NRT, false>(st, q, ps, pbeg, lo, hi);
+  for (int b = 0; b < nblk; ++b) {
+    const int pa = pbeg + 2 * b;
+    const int cur = (b & 1) * 2;
+    // The compiler does not track global -> LDS loads: wait for them here.
+    // The only vector-memory operations in flight are this block's page loads
+    // (the next block's are issued below, after the reads).
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __builtin_amdgcn_sched_barrier(0);
+    PageRegs<D> c0, c1;
+    lds_page<D>(c0, ring.ring[wv][cur], lane, lg);
+    lds_page<D>(c1, ring.ring[wv][cur + 1], lane, lg);
+    int pid0, pid1;
+    const bool ok0 = page_ok(pa, pid0), ok1 = page_ok(pa + 1, pid1);
+    if (b + 1 < nblk) issue_block(pa + 2, 2 - cur);  // next block flies during compute
+    attend_block_any<D, QS, NRT>(st, q, c0, c1, ok0, ok1, pa * kPageTokens, lo, hi, lg);
+  }
 
-  // ---- merge the wavefronts of the workgroup through LDS ----
-  __shared__ float sm_m[kAttnWaves][32];
-  __shared__ float sm_l[kAttnWaves][32];
-  __shared__ f32x4 sm_acc[kAttnWaves - 1][NRT][VT][64];
-  __shared__ int sm_last;
+  // ---- merge the W wavefronts of the workgroup through LDS (pairwise tree) ----
+  // Every page load into this wavefront's ring has landed before the rings
+  // are reused below (vmcnt(0); expcnt and lgkmcnt left at their maxima).
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 #pragma unroll
   for (int n = 0; n < NRT; ++n) {
     const float lrow = row_sum4(st.l[n]);
     if (lg == 0) {
-      sm_m[wv][16 * n + li] = st.m[n];
-      sm_l[wv][16 * n + li] = lrow;
+      sm.m[wv][16 * n + li] = st.m[n];
+      sm.l[wv][16 * n + li] = lrow;
     }
   }
-  __syncthreads();
+  __syncthreads();  // also: every wavefront is done with its ring
   float M[NRT], L[NRT];
 #pragma unroll
   for (int n = 0; n < NRT; ++n) {
     const int row = 16 * n + li;
     float mm = kNegInf;
 #pragma unroll
-    for (int x = 0; x < kAttnWaves; ++x) mm = fmaxf(mm, sm_m[x][row]);
+    for (int x = 0; x < W; ++x) mm = fmaxf(mm, sm.m[x][row]);
     const float mu = mm == kNegInf ? 0.0f : mm;
     float ll = 0.0f;
 #pragma unroll
-    for (int x = 0; x < kAttnWaves; ++x) ll += fast_exp2(sm_m[x][row] - mu) * sm_l[x][row];
+    for (int x = 0; x < W; ++x) ll += fast_exp2(sm.m[x][row] - mu) * sm.l[x][row];
     M[n] = mm;
     L[n] = ll;
-    const float fac = st.ev == kNoExp ? 0.0f : ldexp2(fast_exp2(st.m[n] - mu), st.ev - 14);
+    const float fac = st.ev == kNoExp ? 0.0f : ldexp2(fast_exp2(st.m[n] - mu), st.ev - kPvBias);
 #pragma unroll
     for (int t = 0; t < VT; ++t) st.acc[n][t] *= fac;
   }
-  if (wv > 0) {
 #pragma unroll
-    for (int n = 0; n < NRT; ++n)
-#pragma unroll
-      for (int t = 0; t < VT; ++t) sm_acc[wv - 1][n][t][lane] = st.acc[n][t];
-  }
-  __syncthreads();
-  if (wv == 0) {
-#pragma unroll
-    for (int x = 1; x < kAttnWaves; ++x)
+  for (int half = W / 2; half >= 1; half >>= 1) {
+    if (wv >= half && wv < 2 * half) {
 #pragma unroll
       for (int n = 0; n < NRT; ++n)
 #pragma unroll
-        for (int t = 0; t < VT; ++t) st.acc[n][t] += sm_acc[x - 1][n][t][lane];
+        for (int t = 0; t < VT; ++t) ring.acc[wv - half][n][t][lane] = st.acc[n][t];
+    }
+    __syncthreads();
+    if (wv < half) {
+#pragma unroll
+      for (int n = 0; n < NRT; ++n)
+#pragma unroll
+        for (int t = 0; t < VT; ++t) st.acc[n][t] += ring.acc[wv][n][t][lane];
+    }
+    if (half > 1) __syncthreads();
   }
+  if (wv != 0) return;
 
   if (nch == 1) {  // the workgroup saw the whole range: write the output
-    if (wv != 0) return;
 #pragma unroll
     for (int n = 0; n < NRT; ++n) {
       const int row = 16 * n + li;
@@ -544,37 +722,85 @@ __global__ __launch_bounds__(kAttnWaves * 64) void decode_kernel(
     }
     return;
   }
+  // several chunks: write this chunk's partial record for merge_kernel
+  float* rec = ws + ((int64_t)g.ws_begin + ((int64_t)dw.rbl * a.batch + seq) * g.nchunk + chunk) *
+                        ws_record_floats(D);
+#pragma unroll
+  for (int n = 0; n < NRT; ++n) {
+    const int row = 16 * n + li;
+    if (lg == 0) {
+      rec[row] = M[n];
+      rec[32 + row] = L[n];
+    }
+    float* o = rec + 64 + row * D + 4 * lg;
+#pragma unroll
+    for (int t = 0; t < VT; ++t) *reinterpret_cast<f32x4*>(o + 16 * t) = st.acc[n][t];
+  }
+}
 
-  // ---- several chunks: publish this chunk's partial; the last chunk of the
-  // (row block, sequence) to arrive merges them all ----
-  const int64_t mi = (int64_t)g.merge_begin + (int64_t)dw.rbl * a.batch + seq;
-  float* rec0 =
-      ws + ((int64_t)g.ws_begin + ((int64_t)dw.rbl * a.batch + seq) * g.nchunk) * ws_record_floats(D);
-  if (wv == 0) {
-    float* rec = rec0 + (int64_t)chunk * ws_record_floats(D);
+// ---------------------------------------------------------------------------
+// Decode merge: one workgroup = 8 rows of one (row block, sequence); thread t
+// takes row t/32 of them and D/32 consecutive channels.  Partial records:
+// m[32], l[32], acc[32][D] (acc and l relative to exp2(m)).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a,
+                                                    const int32_t* __restrict__ context_lens,
+                                                    const float* __restrict__ ws,
+                                                    float* __restrict__ out) {
+  int w = blockIdx.x >> 2;
+  const int quarter = blockIdx.x & 3;
+  int gi = 0;
+  while (gi < a.num_groups && w >= a.groups[gi].num_rb * a.batch) {
+    w -= a.groups[gi].num_rb * a.batch;
+    ++gi;
+  }
+  if (gi >= a.num_groups) return;
+  const DecodeGroup& g = a.groups[gi];
+  if (g.nchunk <= 1) return;
+  const int rbl = w / a.batch, seq = w % a.batch;
+  const RowBlock& rb = a.rbs[g.first_rb + rbl];
+  const int ctx = clamp_ctx(context_lens[seq], a.max_context, a.max_pages);
+  int lo, hi;
+  decode_range(ctx, g.window, lo, hi);
+  if (hi <= lo) return;
+  const int ppc = g.pages_per_wave * g.waves;
+  const int nch = ((hi - 1) / 16 - lo / 16 + ppc) / ppc;
+  if (nch <= 1) return;
+  const int row = quarter * 8 + (threadIdx.x >> 5), part = threadIdx.x & 31;
+  if (row >= rb.nrows) return;
+  constexpr int PER = D / 32;
+  constexpr int64_t RS = ws_record_floats(D);
+  const float* rec0 =
+      ws + ((int64_t)g.ws_begin + ((int64_t)rbl * a.batch + seq) * g.nchunk) * RS;
+  float mm = kNegInf;
+#pragma unroll 8
+  for (int c = 0; c < nch; ++c) mm = fmaxf(mm, rec0[c * RS + row]);
+  const float mu = mm == kNegInf ? 0.0f : mm;
+  float acc[PER];
 #pragma unroll
-    for (int n = 0; n < NRT; ++n) {
-      const int row = 16 * n + li;
-      if (lg == 0) {
-        rec[row] = M[n];
-        rec[32 + row] = L[n];
-      }
-      float* o = rec + 64 + row * D + 4 * lg;
+  for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
+  float ll = 0.0f;
+#pragma unroll 8
+  for (int c = 0; c < nch; ++c) {
+    const float* rec = rec0 + c * RS;
+    const float f = fast_exp2(rec[row] - mu);
+    ll += f * rec[32 + row];
+    const float* src = rec + 64 + row * D + part * PER;
+    if constexpr (PER == 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(src);
 #pragma unroll
-      for (int t = 0; t < VT; ++t) *reinterpret_cast<f32x4*>(o + 16 * t) = st.acc[n][t];
+      for (int e = 0; e < 4; ++e) acc[e] += f * x[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] += f * src[e];
     }
   }
-  __threadfence();  // release: the record is visible to every XCD before the count
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev = atomicAdd(counters + mi, 1u);
-    sm_last = prev == (uint32_t)(nch - 1);
-  }
-  __syncthreads();
-  if (!sm_last) return;
-  __threadfence();  // acquire: see every other chunk's record
-  merge_records<D>(rec0, nch, rb.nrows, out + out_row0 * D);
-  if (threadIdx.x == 0) atomicExch(counters + mi, 0u);  // ready for the next call
+  const float inv = ll > 0.0f ? 1.0f / ll : 0.0f;
+  float* o = out + (((int64_t)rb.layer * a.batch + seq) * a.num_q_heads + rb.head0 + row) * D +
+             part * PER;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) o[e] = acc[e] * inv;
 }
 
 // ---------------------------------------------------------------------------
@@ -652,7 +878,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void append_kernel(
     const int row = 16 * n + li;
     const float l = row_sum4(st.l[n]);
     if (row >= nrows) continue;
-    const float inv = (l > 0.0f && st.ev != kNoExp) ? ldexp2(1.0f / l, st.ev - 14) : 0.0f;
+    const float inv = (l > 0.0f && st.ev != kNoExp) ? ldexp2(1.0f / l, st.ev - kPvBias) : 0.0f;
     float* o = out + (row0 + row) * D + 4 * lg;
 #pragma unroll
     for (int tt = 0; tt < VT; ++tt) *reinterpret_cast<f32x4*>(o + 16 * tt) = st.acc[n][tt] * inv;
@@ -664,17 +890,28 @@ __global__ __launch_bounds__(kAttnWaves * 64) void append_kernel(
 // ---------------------------------------------------------------------------
 static inline dim3 padded_grid(int total) { return dim3((unsigned)((total + 7) / 8 * 8)); }
 
-template <int D, int QS, int NRT>
-static hipError_t launch_decode_t(const DecodeArgs& a, const DecodePtrs& p, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<D, QS, NRT>), padded_grid(a.total_wgs), dim3(kAttnWaves * 64),
-                     0, stream, a, p.q, p.out, p.pool, p.block_table, p.context_lens, p.ws,
-                     p.counters);
+template <int D, int QS, int NRT, int W>
+static hipError_t launch_decode_t(const DecodeArgs& a, const DecodePtrs& p, bool need_merge,
+                                  hipStream_t stream) {
+  hipLaunchKernelGGL((decode_kernel<D, QS, NRT, W>), padded_grid(a.total_wgs), dim3(W * 64), 0,
+                     stream, a, p.q, p.out, p.pool, p.block_table, p.context_lens, p.ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !need_merge) return e;
+  hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)a.total_merge * 4), dim3(256), 0, stream,
+                     a, p.context_lens, p.ws, p.out);
   return hipGetLastError();
 }
 
-hipError_t launch_decode(int D, bool q_f32, int nrt, const DecodeArgs& a, const DecodePtrs& p,
-                         hipStream_t stream) {
-#define MQA_DEC(DD, QQ, NN) return launch_decode_t<DD, QQ, NN>(a, p, stream)
+template <int D, int QS, int NRT>
+static hipError_t launch_decode_w(int waves, const DecodeArgs& a, const DecodePtrs& p,
+                                  bool need_merge, hipStream_t stream) {
+  if (waves == 8) return launch_decode_t<D, QS, NRT, 8>(a, p, need_merge, stream);
+  return launch_decode_t<D, QS, NRT, 4>(a, p, need_merge, stream);
+}
+
+hipError_t launch_decode(int D, bool q_f32, int nrt, int waves, const DecodeArgs& a,
+                         const DecodePtrs& p, bool need_merge, hipStream_t stream) {
+#define MQA_DEC(DD, QQ, NN) return launch_decode_w<DD, QQ, NN>(waves, a, p, need_merge, stream)
   if (D == 128) {
     if (q_f32) { if (nrt == 1) MQA_DEC(128, 2, 1); MQA_DEC(128, 2, 2); }
     if (nrt == 1) MQA_DEC(128, 1, 1);

@@ -32,8 +32,8 @@ struct DecodeGroup {
   int32_t nchunk;          // chunks per sequence planned for max_context
   int32_t wg_begin;        // first flat workgroup of the group
   int32_t ws_begin;        // first workspace record of the group
-  int32_t merge_begin;     // first merge counter of the group (row blocks x batch before it)
-  int32_t pad;
+  int32_t merge_begin;     // first merge workgroup of the group (row blocks x batch before it)
+  int32_t waves;           // wavefronts per decode workgroup
 };
 
 struct DecodeArgs {
@@ -58,8 +58,7 @@ struct DecodePtrs {
   const uint8_t* pool;
   const int32_t* block_table;
   const int32_t* context_lens;
-  float* ws;            // partial records
-  uint32_t* counters;   // one arrival counter per (row block, sequence), zero between calls
+  float* ws;            // partial records of sequences split into several chunks
 };
 
 struct AppendArgs {
@@ -93,8 +92,8 @@ hipError_t launch_pack(int D, bool bf16, const void* k, const void* v, int64_t n
                        int64_t row_stride, const int64_t* slot_mapping, uint8_t* pool,
                        int64_t num_pages, hipStream_t stream);
 
-hipError_t launch_decode(int D, bool q_f32, int nrt, const DecodeArgs& a, const DecodePtrs& p,
-                         hipStream_t stream);
+hipError_t launch_decode(int D, bool q_f32, int nrt, int waves, const DecodeArgs& a,
+                         const DecodePtrs& p, bool need_merge, hipStream_t stream);
 
 hipError_t launch_append(int D, bool q_f32, int nrt, const AppendArgs& a, const AppendPtrs& p,
                          hipStream_t stream);

@@ -127,9 +127,15 @@ def test_shared_launch_equals_separate_launches():
     g = GpuCase(w)
     q, q64 = q_tensor(w)
     together = g.decode(q).cpu().numpy()
+    want = oracle.decode(q64, w.context_lens, w.layer_slot, w.layer_window, OracleKV(w))
+    assert_parity(together, want, "3 layers in one launch")
     for li in range(3):
         alone = g.decode(q[li:li + 1].contiguous(), [0], [0]).cpu().numpy()
-        np.testing.assert_allclose(together[li], alone[0], rtol=0, atol=2e-6)
+        assert_parity(alone, want[li:li + 1], f"layer {li} alone")
+        # the two launches split the keys into different chunks, so the fp16
+        # P operand is rounded against different running maxima (each within
+        # 2^-12 of |out| of the exact result)
+        np.testing.assert_allclose(together[li], alone[0], rtol=0, atol=1e-3)
 
 
 def test_output_only_written_where_expected():
@@ -146,14 +152,13 @@ def test_output_only_written_where_expected():
 
 
 def test_workspace_reuse_across_calls():
-    """One zero-filled workspace serves many calls: the arrival counters are
-    back at zero after every call (case 2 splits every sequence)."""
+    """One workspace serves many calls (case 2 splits every sequence), and its
+    initial contents do not matter."""
     w = synth.case2()
     g = GpuCase(w)
     q, q64 = q_tensor(w)
     first = g.decode(q).clone()
-    ws_counters = g._ws[:4 * w.batch].clone()
-    assert torch.count_nonzero(ws_counters) == 0
+    g._ws.fill_(0x7F)
     for _ in range(3):
         again = g.decode(q)
         assert torch.equal(first, again)
