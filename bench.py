@@ -287,9 +287,21 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="0: enough for >= 1 GB of KV")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a 1 GiB copy (counter calibration) and exit")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="turn rocprofv3 --pmc runs in DIR into profiles/attention_counters_caseN.json")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch every step from the host instead of replaying HIP graphs")
     args = ap.parse_args()
+
+    if args.copy_probe:
+        copy_probe()
+        return
+    if args.summarize_counters:
+        cmds = open(os.path.join(args.summarize_counters, "commands.txt")).read().splitlines()
+        summarize_counters(args.case, args.summarize_counters, cmds)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -356,10 +368,15 @@ def main():
     print(json.dumps(res), flush=True)
 
 
+def counters_path(case):
+    return os.path.join(ROOT, "profiles", f"attention_counters_case{case}.json")
+
+
 def traffic_from_profile(case, kv_bytes):
-    """HBM bytes per attention call from the committed counter summary, when
-    it was taken on the current kernel sources (else null)."""
-    p = os.path.join(ROOT, "profiles", f"decode_counters_case{case}.json")
+    """HBM bytes per attention call (reads + writes of every kernel the call
+    launches) from the committed counter summary, when it was taken on the
+    current kernel sources (else null)."""
+    p = counters_path(case)
     if not os.path.exists(p):
         return None
     try:
@@ -368,7 +385,72 @@ def traffic_from_profile(case, kv_bytes):
         return None
     if d.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return d.get("traffic_bytes_per_call")
+    return d.get("hbm_bytes_per_call")
+
+
+COPY_BYTES = 1 << 30
+
+
+def copy_probe():
+    """A plain copy of known size (1 GiB read + 1 GiB written), run under the
+    same counters as the attention kernels to scale FETCH_SIZE / WRITE_SIZE
+    into bytes."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("copy probe done")
+
+
+def _read_counters(d):
+    """{kernel name: {counter: [values per dispatch]}} from a rocprofv3 csv dir."""
+    import csv
+    import glob
+    out = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            out.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+    return out
+
+
+def summarize_counters(case, d, cmds):
+    """Turn four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE, each for the
+    copy probe and for the case) into HBM bytes per attention call."""
+    def per_dispatch(run, counter, pred):
+        data = _read_counters(os.path.join(d, run))
+        vals = [v for k, cs in data.items() if pred(k) for v in cs.get(counter, [])]
+        return vals
+    is_copy = lambda k: "copy" in k.lower() or "elementwise" in k.lower()
+    fc = per_dispatch("fetch_copy", "FETCH_SIZE", is_copy)
+    wc = per_dispatch("write_copy", "WRITE_SIZE", is_copy)
+    fetch_scale = COPY_BYTES / max(fc)      # bytes per counter unit (largest = the 1 GiB copy)
+    write_scale = COPY_BYTES / max(wc)
+    out = {"case": case, "kernel_source_hash": kernel_source_hash(), "commands": cmds,
+           "copy_fetch_units": max(fc), "copy_write_units": max(wc),
+           "fetch_bytes_per_unit": fetch_scale, "write_bytes_per_unit": write_scale,
+           "kernels": {}}
+    total = 0.0
+    for run, counter, scale in (("fetch_case", "FETCH_SIZE", fetch_scale),
+                                ("write_case", "WRITE_SIZE", write_scale)):
+        for k, cs in _read_counters(os.path.join(d, run)).items():
+            if not any(t in k for t in ("decode_kernel", "merge_kernel", "append_kernel")):
+                continue
+            v = cs.get(counter, [])
+            if not v:
+                continue
+            name = k.split("(")[0].replace("void ", "")
+            mean = float(np.mean(v))
+            out["kernels"].setdefault(name, {})[counter] = {"mean_units": mean,
+                                                             "bytes": mean * scale,
+                                                             "dispatches": len(v)}
+            total += mean * scale
+    out["hbm_bytes_per_call"] = total
+    os.makedirs(os.path.dirname(counters_path(case)), exist_ok=True)
+    json.dump(out, open(counters_path(case), "w"), indent=1)
+    log(f"wrote {counters_path(case)}: {total / 1e6:.2f} MB per call")
 
 
 if __name__ == "__main__":

@@ -101,7 +101,8 @@ struct DecodePlan {
   DecodeArgs args;
   int nrt = 2;
   size_t ws_bytes = 0;        // partial records
-  int waves = 8;              // wavefronts per decode workgroup
+  int waves = 4;              // wavefronts per decode workgroup
+  int ring = 4;               // blocks of two pages each wavefront keeps in flight
   bool need_merge = false;
   int rc = MQA_OK;
 };
@@ -112,7 +113,7 @@ int target_workgroups() {
   static const int v = [] {
     const char* e = getenv("MQA_DECODE_TARGET_WGS");
     const int t = e ? atoi(e) : 0;
-    return t > 0 ? t : 384;
+    return t > 0 ? t : 256;
   }();
   return v;
 }
@@ -121,7 +122,16 @@ int decode_waves() {
   static const int v = [] {
     const char* e = getenv("MQA_DECODE_WAVES");
     const int t = e ? atoi(e) : 0;
-    return t == 8 ? 8 : 4;
+    return t == 4 ? 4 : 8;
+  }();
+  return v;
+}
+
+int decode_ring() {
+  static const int v = [] {
+    const char* e = getenv("MQA_DECODE_RING");
+    const int t = e ? atoi(e) : 0;
+    return (t >= 2 && t <= 4) ? t : 4;
   }();
   return v;
 }
@@ -179,6 +189,7 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
     total_pages += max_np[g] * (int64_t)members[g].size() * head_blocks * batch;
   }
   p.waves = decode_waves();
+  p.ring = p.waves == 8 ? 2 : decode_ring();
   int ppw = forced_pages_per_wave();
   if (ppw <= 0) {
     const double x = (double)total_pages / ((double)target_workgroups() * p.waves);
@@ -331,8 +342,8 @@ int mqa_decode_attn(const void* q, mqa_dtype q_dtype, float* out, const mqa_kv_p
   ptrs.block_table = block_table;
   ptrs.context_lens = context_lens;
   ptrs.ws = p.ws_bytes ? static_cast<float*>(workspace) : nullptr;
-  hipError_t e = launch_decode(pool->head_dim, q_dtype == MQA_F32, p.nrt, p.waves, a, ptrs,
-                               p.need_merge, static_cast<hipStream_t>(stream));
+  hipError_t e = launch_decode(pool->head_dim, q_dtype == MQA_F32, p.nrt, p.waves, p.ring, a,
+                               ptrs, p.need_merge, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mqa_decode_attn launch");
   return ok();
 }

@@ -80,8 +80,9 @@ __device__ __forceinline__ void zero_page(PageRegs<D>& r) {
 // ---------------------------------------------------------------------------
 template <int D, int QS, int NRT>
 struct QOps {
-  f16x8 q[NRT][QS][Geo<D>::KSTEPS];
-  float crow[NRT];  // 2^(E-15) * scale * log2(e): undoes the row's prescale
+  static constexpr int KS8 = D / 64;  // 16x16x64 int8 steps over the channels
+  u32x4 q8[NRT][2][KS8];               // [row tile][hi, lo][step]: 16 int8 per lane
+  float crow[NRT];  // 2^(E-14) * scale * log2(e): undoes the row's fixed-point scale
 };
 
 // Raw query registers of one wavefront: rows 16n + li, channels lg*CH .. +CH.
@@ -109,9 +110,10 @@ __device__ __forceinline__ void load_q_raw(QRaw<D, QS, NRT>& r, const void* __re
   }
 }
 
-// Turn the raw rows into matrix-core operands: scale each row by a power of
-// two so that its largest |element| lies in [2^14, 2^15), then round to fp16
-// (exact for bf16 input; fp32 input becomes a sum of two fp16 terms).
+// Turn the raw rows into int8 matrix-core operands: scale each row by a power
+// of two so that its largest |element| lies in [2^13, 2^14), round to an
+// integer and split it into two int8 halves (split_q15).  Lane (i, g) owns
+// row i's channels g*CH .. g*CH+CH-1, exactly its B-operand bytes.
 template <int D, int QS, int NRT>
 __device__ __forceinline__ void convert_q(QOps<D, QS, NRT>& o, const QRaw<D, QS, NRT>& r,
                                           float scale_log2, int nrows, int li) {
@@ -140,19 +142,19 @@ __device__ __forceinline__ void convert_q(QOps<D, QS, NRT>& o, const QRaw<D, QS,
 #pragma unroll
     for (int c = 0; c < CH; ++c) a = fmaxf(a, fabsf(x[c]));
     a = row_max4(a);
-    const int E = a > 0.0f ? max(frexp_exp(a), -100) : 15;
-    const float sc = ldexp2(1.0f, 15 - E);
-    o.crow[n] = ldexp2(scale_log2, E - 15);
+    const int E = a > 0.0f ? max(frexp_exp(a), -100) : 14;
+    const float sc = ldexp2(1.0f, 14 - E);
+    o.crow[n] = ldexp2(scale_log2, E - 14);
 #pragma unroll
-    for (int s = 0; s < Geo<D>::KSTEPS; ++s) {
+    for (int h = 0; h < QOps<D, QS, NRT>::KS8; ++h)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float y = x[8 * s + e] * sc;
-        const _Float16 h1 = (_Float16)y;
-        o.q[n][0][s][e] = h1;
-        if constexpr (QS == 2) o.q[n][1][s][e] = (_Float16)(y - (float)h1);
+      for (int d = 0; d < 4; ++d) {
+        int hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) split_q15(x[16 * h + 4 * d + e] * sc, hi[e], lo[e]);
+        o.q8[n][0][h][d] = pack_i8x4(hi[0], hi[1], hi[2], hi[3]);
+        o.q8[n][1][h][d] = pack_i8x4(lo[0], lo[1], lo[2], lo[3]);
       }
-    }
   }
 }
 
@@ -195,24 +197,25 @@ __device__ __forceinline__ void attend_block(WaveState<D, NRT>& st, const QOps<D
                                              const PageRegs<D>& p0, const PageRegs<D>& p1,
                                              bool ok0, bool ok1, int pos0, int lo, int hi,
                                              int lg) {
-  constexpr int KS = Geo<D>::KSTEPS;
-  // S^T for both pages: lane (i, g) gets the scores of keys 4g..4g+3 for row i.
+  constexpr int KS8 = D / 64;
+  // S^T for both pages on the int8 matrix cores: the K codes are the A operand
+  // as stored (lane (i, g): token i, 16 channels per step); q's two int8
+  // halves are B.  Lane (i, g) gets the scores of keys 4g..4g+3 for row i.
   f32x4 s[NRT][2];
 #pragma unroll
-  for (int n = 0; n < NRT; ++n) s[n][0] = s[n][1] = f32x4{0, 0, 0, 0};
+  for (int n = 0; n < NRT; ++n)
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const PageRegs<D>& P = u ? p1 : p0;
+    for (int u = 0; u < 2; ++u) {
+      const PageRegs<D>& P = u ? p1 : p0;
+      i32x4 shi = i32x4{0, 0, 0, 0}, slo = i32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int h = ks >> 1, dw = (ks & 1) * 2;
-      const f16x8 kop = i8x8_to_f16x8(P.k[h][dw], P.k[h][dw + 1]);
+      for (int h = 0; h < KS8; ++h) {
+        shi = mma_i8(P.k[h], q.q8[n][0][h], shi);
+        slo = mma_i8(P.k[h], q.q8[n][1][h], slo);
+      }
 #pragma unroll
-      for (int n = 0; n < NRT; ++n)
-#pragma unroll
-        for (int qs = 0; qs < QS; ++qs) s[n][u] = mma16(kop, q.q[n][qs][ks], s[n][u]);
+      for (int r = 0; r < 4; ++r) s[n][u][r] = (float)((shi[r] << 8) + slo[r]);
     }
-  }
 
   bool valid[2][4];
 #pragma unroll
@@ -454,18 +457,21 @@ __device__ __forceinline__ void lds_page(PageRegs<D>& r, const uint8_t* lds_slot
 // final merge reuses once every page has been consumed.
 template <int D, int QS, int NRT, int W>
 struct DecodeQLds {
-  static constexpr int KS = Geo<D>::KSTEPS;
-  f16x8 q[NRT][QS][KS][64];
+  static constexpr int KS8 = D / 64;
+  u32x4 q8[NRT][2][KS8][64];
   float crow[32];
   float m[W][32];
   float l[W][32];
 };
-template <int D, int NRT, int W>
+template <int D, int NRT, int W, int RB>
 union DecodeRingLds {
-  static constexpr int RING = 4;
-  uint8_t ring[W][RING][lds_slot_bytes<D>()];
+  uint8_t ring[W][2 * RB][lds_slot_bytes<D>()];  // RB blocks of two pages per wavefront
   f32x4 acc[W / 2][NRT][Geo<D>::VT][64];
 };
+
+// s_waitcnt immediate for "at most n vector-memory operations outstanding"
+// (expcnt and lgkmcnt left at their maxima; vmcnt's 6 bits are split 4 + 2).
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
 
 // The block's query rows staged into fp16 matrix-core operands in LDS, once
 // for all W wavefronts: wavefront w takes rows 4w..4w+3, 4w+4W.., 16 lanes per
@@ -514,8 +520,11 @@ struct StageQ {
     const int sub = lane >> 4, part = lane & 15;
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
-      const int row = min(wv * 4 + ps * 4 * W + sub, 16 * NRT - 1);
-      const bool live = row < nrows && wv * 4 + ps * 4 * W < 16 * NRT;
+      // wavefronts past the block's rows (W = 8 with 16 rows) have nothing to
+      // stage and must not write (they would clobber another row's operands)
+      if (wv * 4 + ps * 4 * W >= 16 * NRT) break;  // wave-uniform
+      const int row = wv * 4 + ps * 4 * W + sub;
+      const bool live = row < nrows;
       float x[PER];
       if constexpr (QS == 1) {
 #pragma unroll
@@ -535,36 +544,40 @@ struct StageQ {
       }
 #pragma unroll
       for (int off = 1; off < 16; off <<= 1) a = fmaxf(a, __shfl_xor(a, off));
-      const int E = a > 0.0f ? max(frexp_exp(a), -100) : 15;
-      const float sc = ldexp2(1.0f, 15 - E);
-      if (part == 0) sm.crow[row] = ldexp2(scale_log2, E - 15);
-      // operand slot of (row, channels c0..c0+PER-1): tile n, lane (li, lg), step ks
+      const int E = a > 0.0f ? max(frexp_exp(a), -100) : 14;
+      const float sc = ldexp2(1.0f, 14 - E);
+      if (part == 0) sm.crow[row] = ldexp2(scale_log2, E - 14);
+      // operand bytes of (row, channels c0..c0+PER-1): tile n, lane (li, lg),
+      // step h, byte offset e0 inside the lane's 16 bytes
       const int c0 = part * PER;
       const int n = row >> 4, li = row & 15;
-      const int lg = c0 / CH, ks = (c0 % CH) >> 3, e0 = c0 & 7;
-      _Float16 h1[PER], h2[PER];
+      const int lg = c0 / CH, h = (c0 % CH) >> 4, e0 = c0 & 15;
+      uint32_t hw[PER / 4], lw[PER / 4];
 #pragma unroll
-      for (int e = 0; e < PER; ++e) {
-        const float y = x[e] * sc;
-        h1[e] = (_Float16)y;
-        h2[e] = (_Float16)(y - (float)h1[e]);
+      for (int d = 0; d < PER / 4; ++d) {
+        int hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) split_q15(x[4 * d + e] * sc, hi[e], lo[e]);
+        hw[d] = pack_i8x4(hi[0], hi[1], hi[2], hi[3]);
+        lw[d] = pack_i8x4(lo[0], lo[1], lo[2], lo[3]);
       }
+      uint32_t* dh = reinterpret_cast<uint32_t*>(&sm.q8[n][0][h][16 * lg + li]) + e0 / 4;
+      uint32_t* dl = reinterpret_cast<uint32_t*>(&sm.q8[n][1][h][16 * lg + li]) + e0 / 4;
+      if constexpr (PER == 8) {
+        *reinterpret_cast<u32x2*>(dh) = u32x2{hw[0], hw[1]};
+        *reinterpret_cast<u32x2*>(dl) = u32x2{lw[0], lw[1]};
+      } else {
 #pragma unroll
-      for (int qs = 0; qs < QS; ++qs) {
-        const _Float16* h = qs == 0 ? h1 : h2;
-        if constexpr (PER == 8) {
-          sm.q[n][qs][ks][16 * lg + li] = f16x8{h[0], h[1], h[2], h[3], h[4], h[5], h[6], h[7]};
-        } else {
-          _Float16* d = reinterpret_cast<_Float16*>(&sm.q[n][qs][ks][16 * lg + li]) + e0;
-#pragma unroll
-          for (int e = 0; e < PER; ++e) d[e] = h[e];
+        for (int d = 0; d < PER / 4; ++d) {
+          dh[d] = hw[d];
+          dl[d] = lw[d];
         }
       }
     }
   }
 };
 
-template <int D, int QS, int NRT, int W>
+template <int D, int QS, int NRT, int W, int RB>
 __global__ __launch_bounds__(W * 64) void decode_kernel(
     const DecodeArgs a, const void* __restrict__ qp, float* __restrict__ out,
     const uint8_t* __restrict__ pool, const int32_t* __restrict__ block_table,
@@ -572,7 +585,10 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(
   constexpr int VT = Geo<D>::VT;
   constexpr int KS = Geo<D>::KSTEPS;
   __shared__ DecodeQLds<D, QS, NRT, W> sm;
-  __shared__ DecodeRingLds<D, NRT, W> ring;
+  __shared__ DecodeRingLds<D, NRT, W, RB> ring;
+  static_assert(sizeof(DecodeQLds<D, QS, NRT, W>) + sizeof(DecodeRingLds<D, NRT, W, RB>) <= 160 * 1024,
+                "LDS");
+  constexpr int DMA_PER_BLOCK = 2 * (32 * D / 1024 + 1);
   const int w = swizzled_block();
   if (w >= a.total_wgs) return;
   const DecodeWork dw = decode_work(a, w);
@@ -628,7 +644,11 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(
     }
   };
   const int nblk = (pend - pbeg + 1) >> 1;
-  issue_block(pbeg, 0);  // unconditional (a wave without pages loads page 0, unused)
+  // RB-1 blocks ahead, issued unconditionally: a block past the wavefront's
+  // pages loads page 0, unused.  Every block then costs the same number of
+  // loads, so one constant wait count below finds the oldest block landed.
+#pragma unroll
+  for (int i = 0; i < RB - 1; ++i) issue_block(pbeg + 2 * i, 2 * i);
   __builtin_amdgcn_sched_barrier(0);
   sq.store(sm, rb.nrows, a.scale_log2, wv, lane);
   __syncthreads();
@@ -637,34 +657,37 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(
   for (int n = 0; n < NRT; ++n) {
     q.crow[n] = sm.crow[16 * n + li];
 #pragma unroll
-    for (int qs = 0; qs < QS; ++qs)
+    for (int hl = 0; hl < 2; ++hl)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) q.q[n][qs][ks] = sm.q[n][qs][ks][lane];
+      for (int h = 0; h < D / 64; ++h) q.q8[n][hl][h] = sm.q8[n][hl][h][lane];
   }
 
   WaveState<D, NRT> st;
   st.init();
   for (int b = 0; b < nblk; ++b) {
     const int pa = pbeg + 2 * b;
-    const int cur = (b & 1) * 2;
+    const int cur = 2 * (b % RB);
     // The compiler does not track global -> LDS loads: wait for them here.
-    // The only vector-memory operations in flight are this block's page loads
-    // (the next block's are issued below, after the reads).
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    // In flight are blocks b .. b+RB-2 (issued in order): leave the younger
+    // ones outstanding.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((RB - 2) * DMA_PER_BLOCK));
     __builtin_amdgcn_sched_barrier(0);
     PageRegs<D> c0, c1;
     lds_page<D>(c0, ring.ring[wv][cur], lane, lg);
     lds_page<D>(c1, ring.ring[wv][cur + 1], lane, lg);
     int pid0, pid1;
     const bool ok0 = page_ok(pa, pid0), ok1 = page_ok(pa + 1, pid1);
-    if (b + 1 < nblk) issue_block(pa + 2, 2 - cur);  // next block flies during compute
+    // block b+RB-1 into the slots read one iteration ago; flies during compute.
+    // With a 2-block ring every wait is vmcnt(0), so past the last block
+    // nothing needs issuing; deeper rings keep the per-block count constant.
+    if (RB > 2 || b + 1 < nblk) issue_block(pa + 2 * (RB - 1), 2 * ((b + RB - 1) % RB));
     attend_block_any<D, QS, NRT>(st, q, c0, c1, ok0, ok1, pa * kPageTokens, lo, hi, lg);
   }
 
   // ---- merge the W wavefronts of the workgroup through LDS (pairwise tree) ----
   // Every page load into this wavefront's ring has landed before the rings
-  // are reused below (vmcnt(0); expcnt and lgkmcnt left at their maxima).
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+  // are reused below.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 #pragma unroll
   for (int n = 0; n < NRT; ++n) {
     const float lrow = row_sum4(st.l[n]);
@@ -890,10 +913,10 @@ __global__ __launch_bounds__(kAttnWaves * 64) void append_kernel(
 // ---------------------------------------------------------------------------
 static inline dim3 padded_grid(int total) { return dim3((unsigned)((total + 7) / 8 * 8)); }
 
-template <int D, int QS, int NRT, int W>
+template <int D, int QS, int NRT, int W, int RB>
 static hipError_t launch_decode_t(const DecodeArgs& a, const DecodePtrs& p, bool need_merge,
                                   hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<D, QS, NRT, W>), padded_grid(a.total_wgs), dim3(W * 64), 0,
+  hipLaunchKernelGGL((decode_kernel<D, QS, NRT, W, RB>), padded_grid(a.total_wgs), dim3(W * 64), 0,
                      stream, a, p.q, p.out, p.pool, p.block_table, p.context_lens, p.ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !need_merge) return e;
@@ -902,16 +925,19 @@ static hipError_t launch_decode_t(const DecodeArgs& a, const DecodePtrs& p, bool
   return hipGetLastError();
 }
 
+// waves x ring depth: (8, 2), (4, 2), (4, 3), (4, 4) -- each fits the 160 KiB LDS
 template <int D, int QS, int NRT>
-static hipError_t launch_decode_w(int waves, const DecodeArgs& a, const DecodePtrs& p,
+static hipError_t launch_decode_w(int waves, int ring, const DecodeArgs& a, const DecodePtrs& p,
                                   bool need_merge, hipStream_t stream) {
-  if (waves == 8) return launch_decode_t<D, QS, NRT, 8>(a, p, need_merge, stream);
-  return launch_decode_t<D, QS, NRT, 4>(a, p, need_merge, stream);
+  if (waves == 8) return launch_decode_t<D, QS, NRT, 8, 2>(a, p, need_merge, stream);
+  if (ring == 4) return launch_decode_t<D, QS, NRT, 4, 4>(a, p, need_merge, stream);
+  if (ring == 3) return launch_decode_t<D, QS, NRT, 4, 3>(a, p, need_merge, stream);
+  return launch_decode_t<D, QS, NRT, 4, 2>(a, p, need_merge, stream);
 }
 
-hipError_t launch_decode(int D, bool q_f32, int nrt, int waves, const DecodeArgs& a,
+hipError_t launch_decode(int D, bool q_f32, int nrt, int waves, int ring, const DecodeArgs& a,
                          const DecodePtrs& p, bool need_merge, hipStream_t stream) {
-#define MQA_DEC(DD, QQ, NN) return launch_decode_w<DD, QQ, NN>(waves, a, p, need_merge, stream)
+#define MQA_DEC(DD, QQ, NN) return launch_decode_w<DD, QQ, NN>(waves, ring, a, p, need_merge, stream)
   if (D == 128) {
     if (q_f32) { if (nrt == 1) MQA_DEC(128, 2, 1); MQA_DEC(128, 2, 2); }
     if (nrt == 1) MQA_DEC(128, 1, 1);

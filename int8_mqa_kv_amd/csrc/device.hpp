@@ -13,6 +13,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLog2e = 1.4426950408889634f;
@@ -56,17 +57,53 @@ __device__ __forceinline__ f32x4 mma16(const f16x8& a, const f16x8& b, const f32
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// Reductions across the four lanes i, i+16, i+32, i+48 (one matrix row).
-__device__ __forceinline__ float row_max4(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+// D = A.B + C on one 16x16x64 int8 tile, int32 accumulate (exact).  Lane l
+// (i = l % 16, g = l / 16) supplies A[i][16g..16g+15] and B[16g..16g+15][i]
+// (16 bytes each) and receives D[4g..4g+3][i].
+__device__ __forceinline__ i32x4 mma_i8(const u32x4& a, const u32x4& b, const i32x4& c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(bitcast<i32x4>(a), bitcast<i32x4>(b), c, 0, 0, 0);
 }
-__device__ __forceinline__ float row_sum4(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+
+// A query element as a 15-bit fixed-point integer split into two int8 halves:
+// v = rint(y) with |y| < 2^14, hi = (v + 128) >> 8 in [-64, 64],
+// lo = v - 256*hi in [-128, 127]; v = 256*hi + lo exactly.
+__device__ __forceinline__ void split_q15(float y, int& hi, int& lo) {
+  const int v = (int)__builtin_rintf(y);
+  hi = (v + 128) >> 8;
+  lo = v - (hi << 8);
 }
+
+__device__ __forceinline__ uint32_t pack_i8x4(int a, int b, int c, int d) {
+  return (uint32_t)(a & 255) | ((uint32_t)(b & 255) << 8) | ((uint32_t)(c & 255) << 16) |
+         ((uint32_t)d << 24);
+}
+
+// Reductions across the four lanes i, i+16, i+32, i+48 (one matrix row) with
+// the gfx950 lane swaps: permlane16_swap(x, x) returns {x[l], x[l^16]} in some
+// order on every lane (permlane32_swap likewise for l^32), so one swap and one
+// max or add combine a lane with its partner without going through LDS.
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(bitcast<uint32_t>(x), bitcast<uint32_t>(x), false,
+                                                  false);
+  return fmaxf(bitcast<float>((uint32_t)r[0]), bitcast<float>((uint32_t)r[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(bitcast<uint32_t>(x), bitcast<uint32_t>(x), false,
+                                                  false);
+  return fmaxf(bitcast<float>((uint32_t)r[0]), bitcast<float>((uint32_t)r[1]));
+}
+__device__ __forceinline__ float xor16_add(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(bitcast<uint32_t>(x), bitcast<uint32_t>(x), false,
+                                                  false);
+  return bitcast<float>((uint32_t)r[0]) + bitcast<float>((uint32_t)r[1]);
+}
+__device__ __forceinline__ float xor32_add(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(bitcast<uint32_t>(x), bitcast<uint32_t>(x), false,
+                                                  false);
+  return bitcast<float>((uint32_t)r[0]) + bitcast<float>((uint32_t)r[1]);
+}
+__device__ __forceinline__ float row_max4(float x) { return xor32_max(xor16_max(x)); }
+__device__ __forceinline__ float row_sum4(float x) { return xor32_add(xor16_add(x)); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

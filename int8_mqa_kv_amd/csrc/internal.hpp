@@ -92,7 +92,7 @@ hipError_t launch_pack(int D, bool bf16, const void* k, const void* v, int64_t n
                        int64_t row_stride, const int64_t* slot_mapping, uint8_t* pool,
                        int64_t num_pages, hipStream_t stream);
 
-hipError_t launch_decode(int D, bool q_f32, int nrt, int waves, const DecodeArgs& a,
+hipError_t launch_decode(int D, bool q_f32, int nrt, int waves, int ring, const DecodeArgs& a,
                          const DecodePtrs& p, bool need_merge, hipStream_t stream);
 
 hipError_t launch_append(int D, bool q_f32, int nrt, const AppendArgs& a, const AppendPtrs& p,
