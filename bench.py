@@ -335,7 +335,7 @@ def main():
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int8 KV codes, fp16 matrix-core operands, fp32 accumulate",
+        "dtype": "int8",
         "data": "synthetic (seeded)",
         "config": {"workload": f"case {w.case}: {w.name}", "batch": w.batch,
                    "num_q_heads": w.num_q_heads, "kv_heads": 1, "head_dim": w.head_dim,

@@ -18,6 +18,11 @@ import os
 from typing import Optional, Sequence
 
 import numpy as np
+# torch ships its own HIP runtime under the same soname as ROCm's
+# (libamdhip64.so.7).  Loading torch first makes the library below bind to
+# that one runtime; loading the library first would bring up a second runtime
+# that sees no device once torch initialises its own.
+import torch  # noqa: F401  (import order matters, see above)
 
 __all__ = [
     "PAGE_TOKENS", "MQAError", "KVPool", "lib", "page_bytes", "kv_bytes_per_token",
