@@ -5,18 +5,21 @@
 
 One step is one pass of the whole hot path over one batch of synthetic input
 already resident in HBM:
-  decode cases (1-3): kv_pack_int8 of the current token of every sequence,
-                      then mqa_decode_attn over every layer of the case;
+  decode cases (1-3): mqa_decode_step -- the current token of every sequence
+                      coded to int8 and stored, and decode attention over
+                      every layer of the case, in one launch;
   append case (4):    kv_pack_int8 of the appended chunk into every slot, then
                       mqa_append_attn over all 12 layers.
 Inputs are rotated over replicas (pool, q, out, new rows) whose attended bytes
 together exceed 1 GB, so the 256 MB Infinity Cache and the L2s cannot serve a
 step from the previous one.  By default the steps are replayed from HIP graphs
 (one step per replica per graph), as a serving loop replays its captured
-decode step; HIP events on the replay stream time the region.  The attention
-calls alone are timed the same way from a graph of only them: that average is
-the roofline's launch duration.  --no-graph launches every call from the host
-instead (then the host's launch rate, not the GPU, limits the small cases).
+decode step; HIP events on the replay stream time the region.  The roofline's
+launch duration is that of the dominant kernel: the decode step's single
+kernel (so the step time), or for the append case the attention call timed
+alone from a graph of only those calls.  --no-graph launches every call from
+the host instead (then the host's launch rate, not the GPU, limits the small
+cases).
 
 Prints one JSON line.  ``value`` is int8 KV GB/s of the whole step: the KV
 bytes the step must stream (codes + fp32 scales of every attended key of every
@@ -40,6 +43,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak, published
 METRIC = "int8 KV GB/s (% of HBM peak) and decode tokens/s, MQA attention, 1 GPU"
 KERNEL_SOURCES = ["int8_mqa_kv_amd/csrc/attn.hip", "int8_mqa_kv_amd/csrc/device.hpp",
+                  "int8_mqa_kv_amd/csrc/pack.hip",
                   "int8_mqa_kv_amd/csrc/internal.hpp", "int8_mqa_kv_amd/csrc/layout.hpp",
                   "int8_mqa_kv_amd/csrc/api.hip"]
 
@@ -91,7 +95,8 @@ def setup(w, replicas, torch, mk, synth):
             if n >= (1 << 20):
                 flush()
     flush()
-    # the rows the step packs: the current token (decode) or the chunk (append)
+    # the rows the step stores: the current token of every (slot, sequence),
+    # [num_slots, B, D] (decode), or the chunk, [tokens, D] + slot mapping (append)
     nk, nv, nsm = [], [], []
     for s in range(w.num_slots):
         for b in range(w.batch):
@@ -104,6 +109,9 @@ def setup(w, replicas, torch, mk, synth):
     new_k = torch.from_numpy(np.concatenate(nk)).to(dev)
     new_v = torch.from_numpy(np.concatenate(nv)).to(dev)
     new_sm = torch.from_numpy(np.concatenate(nsm)).to(dev)
+    if w.kind == "decode":
+        new_k = new_k.view(w.num_slots, w.batch, w.head_dim)
+        new_v = new_v.view(w.num_slots, w.batch, w.head_dim)
     qf = w.q_f32()
     if w.q_dtype == "bf16":
         q0 = torch.from_numpy(synth.f32_to_bf16_bits(qf).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -142,6 +150,15 @@ def attn_call(w, st, R, mk):
 
 
 def step(w, st, R, mk, ev=None):
+    """One step; ``ev`` brackets the dominant kernel's launch."""
+    if w.kind == "decode":
+        if ev is not None:
+            ev[0].record()
+        mk.mqa_decode_step(R.q, R.out, R.k, R.v, R.pool, st["bt"], st["ctx"], w.max_context,
+                           w.layer_slot, w.layer_window, workspace=st["ws"])
+        if ev is not None:
+            ev[1].record()
+        return
     mk.kv_pack_int8(R.k, R.v, st["sm"], R.pool)
     if ev is not None:
         ev[0].record()
@@ -214,7 +231,7 @@ def cpu_baseline(w, kv_bytes_step, budget_s):
 
 
 def time_eager(w, st, R, reps, mk, torch, args):
-    """Host-launched steps; events around every attention call."""
+    """Host-launched steps; events around every dominant kernel."""
     for i in range(args.warmup):
         step(w, st, R[i % reps], mk)
     torch.cuda.synchronize()
@@ -234,8 +251,9 @@ def time_graphs(w, st, R, reps, mk, torch, args):
     """Steps replayed from HIP graphs (one graph holds one step per replica),
     as a serving loop replays its captured decode step.  The timed region is
     exactly ``steps`` steps: full-graph replays plus one graph for the
-    remainder.  The attention calls alone are timed the same way from a graph
-    holding only them."""
+    remainder.  The attention calls alone (mqa_decode_attn without the
+    current token's store, or mqa_append_attn) are timed the same way from a
+    graph holding only them."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):          # warm up (and plan) outside capture
@@ -328,6 +346,10 @@ def main():
     else:
         ms_step, attn_ms = time_graphs(w, st, R, reps, mk, torch, args)
     log(f"step {ms_step * 1e3:.2f} us, attention call {attn_ms * 1e3:.2f} us")
+    # the dominant kernel: the decode step is one kernel, so its launch time
+    # is the step time; for append it is the attention call
+    # (host launches: the events around each step's kernel)
+    dom_ms = ms_step if (w.kind == "decode" and not args.no_graph) else attn_ms
 
     tokens = int(w.q_lens.sum()) * w.num_layers
     value = kv_bytes / (ms_step * 1e-3) / 1e9
@@ -348,16 +370,19 @@ def main():
         "kv_bytes_per_step": kv_bytes,
     }
     if w.kind == "decode":
-        achieved = kv_bytes / (attn_ms * 1e-3) / 1e9
+        achieved = kv_bytes / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
     else:
         fl = attention_flops(w)
-        achieved = fl / (attn_ms * 1e-3) / 1e12
+        achieved = fl / (dom_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4)}
-    roof["kernel"] = "mqa_decode_attn" if w.kind == "decode" else "mqa_append_attn"
-    roof["avg_launch_us"] = round(attn_ms * 1e3, 3)
+    roof["kernel"] = ("decode_kernel (mqa_decode_step: store + attention, one launch)"
+                      if w.kind == "decode" else "append_kernel (mqa_append_attn)")
+    roof["avg_launch_us"] = round(dom_ms * 1e3, 3)
+    if w.kind == "decode" and not args.no_graph:
+        roof["attention_only_us"] = round(attn_ms * 1e3, 3)
     roof["timing"] = ("host launches, events around each call" if args.no_graph else
                       "HIP graph replay of back-to-back calls, events around the replays")
     roof["traffic"] = traffic_from_profile(w.case, kv_bytes)
@@ -373,9 +398,9 @@ def counters_path(case):
 
 
 def traffic_from_profile(case, kv_bytes):
-    """HBM bytes per attention call (reads + writes of every kernel the call
-    launches) from the committed counter summary, when it was taken on the
-    current kernel sources (else null)."""
+    """HBM bytes per launch of the dominant kernel (reads + writes) from the
+    committed counter summary, when it was taken on the current kernel
+    sources (else null)."""
     p = counters_path(case)
     if not os.path.exists(p):
         return None
@@ -418,7 +443,8 @@ def _read_counters(d):
 
 def summarize_counters(case, d, cmds):
     """Turn four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE, each for the
-    copy probe and for the case) into HBM bytes per attention call."""
+    copy probe and for the case) into HBM bytes per launch of the dominant
+    kernel."""
     def per_dispatch(run, counter, pred):
         data = _read_counters(os.path.join(d, run))
         vals = [v for k, cs in data.items() if pred(k) for v in cs.get(counter, [])]
@@ -436,7 +462,7 @@ def summarize_counters(case, d, cmds):
     for run, counter, scale in (("fetch_case", "FETCH_SIZE", fetch_scale),
                                 ("write_case", "WRITE_SIZE", write_scale)):
         for k, cs in _read_counters(os.path.join(d, run)).items():
-            if not any(t in k for t in ("decode_kernel", "merge_kernel", "append_kernel")):
+            if not any(t in k for t in ("decode_kernel", "append_kernel")):
                 continue
             v = cs.get(counter, [])
             if not v:

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MQA_KV_ABI_VERSION 1
+#define MQA_KV_ABI_VERSION 2
 #define MQA_PAGE_TOKENS 16
 
 typedef enum {
@@ -142,11 +142,16 @@ int kv_pack_int8(const void* k, const void* v, mqa_dtype src_dtype,
                  void* stream);
 
 /*
- * Workspace for mqa_decode_attn with the same shape arguments (the host
- * arrays are read).  The workspace holds the softmax partials (max, sum,
- * weighted values) of contexts split across workgroups; a second kernel of
- * the same call merges them.  Returns 0 when none is needed or the arguments
- * are invalid (a following mqa_decode_attn call reports why).
+ * Workspace for mqa_decode_attn / mqa_decode_step with the same shape
+ * arguments (the host arrays are read).  Contexts long enough to be split
+ * across workgroups leave softmax partials (max, sum, weighted values) there;
+ * the workgroup that arrives last merges them inside the same kernel.  The
+ * first 256 KiB of a workspace hold the arrival counters (one per 32-head row
+ * block of a layer and sequence, at most 65536 per call), the partials follow.
+ * Returns 0 when none is needed or the arguments are invalid (a following
+ * call reports why).  The workspace must be zero-filled ONCE before its first
+ * use (e.g. hipMemset after allocation); every call leaves the counters at
+ * zero again, so later calls -- of any shape -- need no clearing.
  */
 size_t mqa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                   int32_t num_layers, const int32_t* layer_slot,
@@ -181,12 +186,44 @@ size_t mqa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
  *                positions (the query's own included).
  *  softmax_scale <= 0 selects 1/sqrt(head_dim).
  *  workspace     at least mqa_decode_workspace_bytes(...) bytes, 256-byte
- *                aligned; contents need no initialisation.  May be NULL when
- *                that size is 0.  Calls sharing one workspace must not
- *                overlap (calls on one stream never do).
+ *                aligned, zero-filled before its first use (see above).  May
+ *                be NULL when that size is 0.  Calls sharing one workspace
+ *                must not overlap (calls on one stream never do).
  * Supported: head_dim 64 or 128; q_dtype MQA_F32 or MQA_BF16; out fp32.
  */
 int mqa_decode_attn(const void* q, mqa_dtype q_dtype, float* out,
+                    const mqa_kv_pool* pool, const int32_t* block_table,
+                    int32_t max_pages_per_seq, const int32_t* context_lens,
+                    int32_t max_context, int32_t batch, int32_t num_q_heads,
+                    int32_t num_layers, int32_t num_slots,
+                    const int32_t* layer_slot, const int32_t* layer_window,
+                    float softmax_scale, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
+ * mqa_decode_step -- kv_pack_int8 of the current token fused into
+ * mqa_decode_attn: one launch stores every slot's new K/V row and runs the
+ * decode attention that reads it.
+ *
+ * Defined by: a new token's K and V are computed once and kept in the cache
+ * (Red Hat page, "Por que o cache KV existe"), as int8 (Character.AI page,
+ * section 05); its query then attends the cache including itself (same
+ * sections as mqa_decode_attn).
+ *
+ *  k_new, v_new  [num_slots][batch][head_dim] of `kv_dtype` (MQA_F32 or
+ *                MQA_BF16): the current token's K and V row of each slot.
+ * For every slot that some layer reads and every sequence b with
+ * context_lens[b] >= 1, the rows of (slot, b) are coded exactly as
+ * kv_pack_int8 codes them and stored at position context_lens[b] - 1, i.e.
+ * page block_table[slot][b][(ctx-1)/16], token (ctx-1)%16 -- the same bytes
+ * kv_pack_int8 followed by mqa_decode_attn would leave -- and `out` equals
+ * what that pair of calls returns.  Rows of slots no layer reads are not
+ * stored.  The page holding the current token must not be shared with
+ * another sequence in the same call.  Other arguments, the workspace and the
+ * error behaviour are those of mqa_decode_attn.
+ */
+int mqa_decode_step(const void* q, mqa_dtype q_dtype, float* out,
+                    const void* k_new, const void* v_new, mqa_dtype kv_dtype,
                     const mqa_kv_pool* pool, const int32_t* block_table,
                     int32_t max_pages_per_seq, const int32_t* context_lens,
                     int32_t max_context, int32_t batch, int32_t num_q_heads,

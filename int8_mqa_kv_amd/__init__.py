@@ -9,6 +9,7 @@ int8_mqa_kv_amd.build``); importing fails loudly when it is not.
 Entry points (same names as the C ABI):
   kv_pack_int8      quantise new K/V rows to int8 + fp32 scales into pages
   mqa_decode_attn   one decode step over the paged int8 cache
+  mqa_decode_step   kv_pack_int8 of the current token fused into mqa_decode_attn
   mqa_append_attn   causal attention of an appended chunk on a cached prefix
 """
 from __future__ import annotations
@@ -26,7 +27,8 @@ import torch  # noqa: F401  (import order matters, see above)
 
 __all__ = [
     "PAGE_TOKENS", "MQAError", "KVPool", "lib", "page_bytes", "kv_bytes_per_token",
-    "page_layout", "kv_pack_int8", "decode_workspace_bytes", "mqa_decode_attn",
+    "page_layout", "kv_pack_int8", "decode_workspace_bytes", "decode_workspace",
+    "mqa_decode_attn", "mqa_decode_step",
     "mqa_append_attn", "slot_mapping_for", "unpack_page_tokens",
 ]
 
@@ -69,6 +71,9 @@ def _load() -> ctypes.CDLL:
     L.mqa_decode_attn.argtypes = [p, ctypes.c_int, p, ctypes.POINTER(_Pool), p, i32, p, i32, i32,
                                   i32, i32, i32, p, p, f32, p, sz, p]
     L.mqa_decode_attn.restype = ctypes.c_int
+    L.mqa_decode_step.argtypes = [p, ctypes.c_int, p, p, p, ctypes.c_int, ctypes.POINTER(_Pool), p,
+                                  i32, p, i32, i32, i32, i32, i32, p, p, f32, p, sz, p]
+    L.mqa_decode_step.restype = ctypes.c_int
     L.mqa_append_attn.argtypes = [p, ctypes.c_int, p, ctypes.POINTER(_Pool), p, i32, p, p, i32,
                                   i32, i32, i32, i32, i32, i32, p, p, f32, p]
     L.mqa_append_attn.restype = ctypes.c_int
@@ -233,13 +238,17 @@ def decode_workspace_bytes(batch: int, num_q_heads: int, layer_slot: Sequence[in
                                               lw.ctypes.data, max_context, head_dim))
 
 
-def mqa_decode_attn(q, out, pool: KVPool, block_table, context_lens, max_context: int,
-                    layer_slot: Sequence[int], layer_window: Sequence[int],
-                    softmax_scale: float = 0.0, workspace=None, stream=None) -> None:
-    """One decode step.  ``q [L, B, Hq, D]`` (fp32/bf16), ``out`` fp32 of the
-    same shape, ``block_table`` int32 [num_slots, B, max_pages],
-    ``context_lens`` int32 [B] (device), ``layer_slot``/``layer_window`` host
-    sequences of length L."""
+def decode_workspace(batch: int, num_q_heads: int, layer_slot: Sequence[int],
+                     layer_window: Sequence[int], max_context: int, head_dim: int,
+                     device="cuda"):
+    """A zero-filled workspace for these decode shapes (None when none is
+    needed).  Zero-fill once; every call leaves it reusable."""
+    n = decode_workspace_bytes(batch, num_q_heads, layer_slot, layer_window, max_context,
+                               head_dim)
+    return _torch().zeros(n, dtype=_torch().uint8, device=device) if n else None
+
+
+def _decode_args(q, out, pool, block_table, context_lens, layer_slot, layer_window, workspace):
     torch = _torch()
     if q.dim() != 4:
         raise ValueError("q must be [L, B, Hq, D]")
@@ -257,12 +266,49 @@ def mqa_decode_attn(q, out, pool: KVPool, block_table, context_lens, max_context
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         ws_ptr, ws_bytes = _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    return (n_layers, batch, hq, ls, lw, ws_ptr, ws_bytes,
+            _dev_ptr(out, "out", torch.float32), _dev_ptr(block_table, "block_table", torch.int32),
+            _dev_ptr(context_lens, "context_lens", torch.int32))
+
+
+def mqa_decode_attn(q, out, pool: KVPool, block_table, context_lens, max_context: int,
+                    layer_slot: Sequence[int], layer_window: Sequence[int],
+                    softmax_scale: float = 0.0, workspace=None, stream=None) -> None:
+    """One decode step.  ``q [L, B, Hq, D]`` (fp32/bf16), ``out`` fp32 of the
+    same shape, ``block_table`` int32 [num_slots, B, max_pages],
+    ``context_lens`` int32 [B] (device), ``layer_slot``/``layer_window`` host
+    sequences of length L, ``workspace`` from :func:`decode_workspace`."""
+    (n_layers, batch, hq, ls, lw, ws_ptr, ws_bytes, out_p, bt_p,
+     cl_p) = _decode_args(q, out, pool, block_table, context_lens, layer_slot, layer_window,
+                          workspace)
     _check(lib.mqa_decode_attn(
-        _dev_ptr(q, "q"), _dtype_code(q), _dev_ptr(out, "out", torch.float32), ctypes.byref(pool.c),
-        _dev_ptr(block_table, "block_table", torch.int32), int(block_table.shape[2]),
-        _dev_ptr(context_lens, "context_lens", torch.int32), int(max_context), batch, hq, n_layers,
+        _dev_ptr(q, "q"), _dtype_code(q), out_p, ctypes.byref(pool.c), bt_p,
+        int(block_table.shape[2]), cl_p, int(max_context), batch, hq, n_layers,
         int(block_table.shape[0]), ls.ctypes.data, lw.ctypes.data, float(softmax_scale), ws_ptr,
         ws_bytes, _stream_ptr(stream)))
+
+
+def mqa_decode_step(q, out, k_new, v_new, pool: KVPool, block_table, context_lens,
+                    max_context: int, layer_slot: Sequence[int], layer_window: Sequence[int],
+                    softmax_scale: float = 0.0, workspace=None, stream=None) -> None:
+    """The current token's K/V (``k_new``, ``v_new`` [num_slots, B, D], fp32 or
+    bf16) stored at position ``context_lens[b] - 1`` of each slot, fused with
+    :func:`mqa_decode_attn` in one launch."""
+    (n_layers, batch, hq, ls, lw, ws_ptr, ws_bytes, out_p, bt_p,
+     cl_p) = _decode_args(q, out, pool, block_table, context_lens, layer_slot, layer_window,
+                          workspace)
+    num_slots = int(block_table.shape[0])
+    want = (num_slots, batch, pool.head_dim)
+    if tuple(k_new.shape) != want or tuple(v_new.shape) != want:
+        raise ValueError(f"k_new and v_new must be {list(want)}")
+    if k_new.dtype != v_new.dtype:
+        raise ValueError("k_new and v_new must have the same dtype")
+    _check(lib.mqa_decode_step(
+        _dev_ptr(q, "q"), _dtype_code(q), out_p, _dev_ptr(k_new, "k_new"),
+        _dev_ptr(v_new, "v_new"), _dtype_code(k_new), ctypes.byref(pool.c), bt_p,
+        int(block_table.shape[2]), cl_p, int(max_context), batch, hq, n_layers, num_slots,
+        ls.ctypes.data, lw.ctypes.data, float(softmax_scale), ws_ptr, ws_bytes,
+        _stream_ptr(stream)))
 
 
 def mqa_append_attn(q, out, pool: KVPool, block_table, context_lens, cu_q_lens, max_context: int,

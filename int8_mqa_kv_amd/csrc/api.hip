@@ -100,15 +100,13 @@ float scale_log2_of(float softmax_scale, int head_dim) {
 struct DecodePlan {
   DecodeArgs args;
   int nrt = 2;
-  size_t ws_bytes = 0;        // partial records
-  int waves = 4;              // wavefronts per decode workgroup
-  int ring = 4;               // blocks of two pages each wavefront keeps in flight
-  bool need_merge = false;
+  size_t ws_bytes = 0;        // partial records + arrival counters
   int rc = MQA_OK;
 };
 
-// Workgroups the planner aims for: a few per compute unit of the 256, so that
-// every CU keeps several pages in flight.
+// Workgroups the planner aims for: one per compute unit of the 256, each with
+// kDecodeWaves wavefronts keeping pages in flight.  MQA_DECODE_TARGET_WGS
+// overrides it (a tuning aid; results do not depend on it beyond rounding).
 int target_workgroups() {
   static const int v = [] {
     const char* e = getenv("MQA_DECODE_TARGET_WGS");
@@ -118,30 +116,14 @@ int target_workgroups() {
   return v;
 }
 
-int decode_waves() {
-  static const int v = [] {
-    const char* e = getenv("MQA_DECODE_WAVES");
-    const int t = e ? atoi(e) : 0;
-    return t == 4 ? 4 : 8;
-  }();
-  return v;
-}
-
-int decode_ring() {
-  static const int v = [] {
-    const char* e = getenv("MQA_DECODE_RING");
-    const int t = e ? atoi(e) : 0;
-    return (t >= 2 && t <= 4) ? t : 4;
-  }();
-  return v;
-}
-
+// MQA_DECODE_PAGES_PER_WAVE fixes the pages each wavefront takes (even, at
+// most 64), another tuning aid; 0 lets the planner choose.
 int forced_pages_per_wave() {
   static const int v = [] {
     const char* e = getenv("MQA_DECODE_PAGES_PER_WAVE");
     int t = e ? atoi(e) : 0;
     if (t > 0 && (t & 1)) ++t;
-    return t;
+    return std::min(t, 64);
   }();
   return v;
 }
@@ -188,21 +170,24 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
     max_np[g] = (span + kPageTokens - 1) / kPageTokens + 1;
     total_pages += max_np[g] * (int64_t)members[g].size() * head_blocks * batch;
   }
-  p.waves = decode_waves();
-  p.ring = p.waves == 8 ? 2 : decode_ring();
   int ppw = forced_pages_per_wave();
   if (ppw <= 0) {
-    const double x = (double)total_pages / ((double)target_workgroups() * p.waves);
+    const double x = (double)total_pages / ((double)target_workgroups() * kDecodeWaves);
     ppw = std::max(2, 2 * (int)llround(x / 2.0));
     ppw = std::min(ppw, 64);  // one register window of page ids per wavefront
   }
 
   int rb = 0;
   int64_t wg = 0, ws = 0, merges = 0;
+  bool split = false;
   for (size_t g = 0; g < keys.size(); ++g) {
     DecodeGroup& G = a.groups[g];
     G.slot = keys[g].first;
     G.window = keys[g].second;
+    // the first group reading a slot stores that slot's current token
+    G.writes_new_kv = 1;
+    for (size_t h = 0; h < g; ++h)
+      if (keys[h].first == G.slot) G.writes_new_kv = 0;
     G.first_rb = rb;
     for (int l : members[g])
       for (int hb = 0; hb < head_blocks; ++hb) {
@@ -213,14 +198,13 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
       }
     G.num_rb = rb - G.first_rb;
     G.pages_per_wave = ppw;
-    G.waves = p.waves;
-    const int64_t ppc = (int64_t)ppw * p.waves;
+    const int64_t ppc = (int64_t)ppw * kDecodeWaves;
     G.nchunk = (int)((max_np[g] + ppc - 1) / ppc);
     G.wg_begin = (int)wg;
     G.ws_begin = (int)ws;
     G.merge_begin = (int)merges;
     wg += (int64_t)G.num_rb * batch * G.nchunk;
-    if (G.nchunk > 1) p.need_merge = true;
+    if (G.nchunk > 1) split = true;
     ws += (int64_t)G.num_rb * batch * G.nchunk;
     merges += (int64_t)G.num_rb * batch;
   }
@@ -231,7 +215,16 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
   a.num_groups = (int)keys.size();
   a.total_wgs = (int)wg;
   a.total_merge = (int)merges;
-  if (p.need_merge) p.ws_bytes = (size_t)ws * ws_record_floats(head_dim) * sizeof(float);
+  if (split) {
+    // the fixed counter prefix, then the partial records
+    if (merges > kDecodeCounters) {
+      p.rc = fail(MQA_ERR_UNSUPPORTED,
+                  "%lld (row block, sequence) pairs with split contexts in one call; at most %lld",
+                  (long long)merges, (long long)kDecodeCounters);
+      return p;
+    }
+    p.ws_bytes = (size_t)(kDecodeCounters + ws * ws_record_floats(head_dim)) * sizeof(float);
+  }
   return p;
 }
 
@@ -309,12 +302,18 @@ size_t mqa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
   return p.rc ? 0 : p.ws_bytes;
 }
 
-int mqa_decode_attn(const void* q, mqa_dtype q_dtype, float* out, const mqa_kv_pool* pool,
-                    const int32_t* block_table, int32_t max_pages_per_seq,
-                    const int32_t* context_lens, int32_t max_context, int32_t batch,
-                    int32_t num_q_heads, int32_t num_layers, int32_t num_slots,
-                    const int32_t* layer_slot, const int32_t* layer_window, float softmax_scale,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by mqa_decode_attn and mqa_decode_step.
+int decode_common(const void* q, mqa_dtype q_dtype, float* out, const void* k_new,
+                  const void* v_new, NewKV nk, const mqa_kv_pool* pool,
+                  const int32_t* block_table, int32_t max_pages_per_seq,
+                  const int32_t* context_lens, int32_t max_context, int32_t batch,
+                  int32_t num_q_heads, int32_t num_layers, int32_t num_slots,
+                  const int32_t* layer_slot, const int32_t* layer_window, float softmax_scale,
+                  void* workspace, size_t workspace_bytes, void* stream, const char* what) {
   int rc = check_attn_common(q, q_dtype, out, pool, block_table, max_pages_per_seq, context_lens,
                              max_context, batch, num_q_heads, num_layers, num_slots, layer_slot,
                              layer_window);
@@ -338,14 +337,52 @@ int mqa_decode_attn(const void* q, mqa_dtype q_dtype, float* out, const mqa_kv_p
   DecodePtrs ptrs;
   ptrs.q = q;
   ptrs.out = out;
-  ptrs.pool = static_cast<const uint8_t*>(pool->base);
+  ptrs.pool = static_cast<uint8_t*>(pool->base);
   ptrs.block_table = block_table;
   ptrs.context_lens = context_lens;
   ptrs.ws = p.ws_bytes ? static_cast<float*>(workspace) : nullptr;
-  hipError_t e = launch_decode(pool->head_dim, q_dtype == MQA_F32, p.nrt, p.waves, p.ring, a,
-                               ptrs, p.need_merge, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "mqa_decode_attn launch");
+  ptrs.k_new = k_new;
+  ptrs.v_new = v_new;
+  hipError_t e = launch_decode(pool->head_dim, q_dtype == MQA_F32, p.nrt, nk, a, ptrs,
+                               static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, what);
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int mqa_decode_attn(const void* q, mqa_dtype q_dtype, float* out, const mqa_kv_pool* pool,
+                    const int32_t* block_table, int32_t max_pages_per_seq,
+                    const int32_t* context_lens, int32_t max_context, int32_t batch,
+                    int32_t num_q_heads, int32_t num_layers, int32_t num_slots,
+                    const int32_t* layer_slot, const int32_t* layer_window, float softmax_scale,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(q, q_dtype, out, nullptr, nullptr, NewKV::kNone, pool, block_table,
+                       max_pages_per_seq, context_lens, max_context, batch, num_q_heads,
+                       num_layers, num_slots, layer_slot, layer_window, softmax_scale, workspace,
+                       workspace_bytes, stream, "mqa_decode_attn launch");
+}
+
+int mqa_decode_step(const void* q, mqa_dtype q_dtype, float* out, const void* k_new,
+                    const void* v_new, mqa_dtype kv_dtype, const mqa_kv_pool* pool,
+                    const int32_t* block_table, int32_t max_pages_per_seq,
+                    const int32_t* context_lens, int32_t max_context, int32_t batch,
+                    int32_t num_q_heads, int32_t num_layers, int32_t num_slots,
+                    const int32_t* layer_slot, const int32_t* layer_window, float softmax_scale,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (kv_dtype != MQA_F32 && kv_dtype != MQA_BF16)
+    return fail(MQA_ERR_UNSUPPORTED, "k_new/v_new dtype %d unsupported", (int)kv_dtype);
+  if (!k_new || !v_new) return fail(MQA_ERR_INVALID, "k_new and v_new must be non-NULL");
+  const size_t esz = kv_dtype == MQA_BF16 ? 2 : 4;
+  if (!aligned(k_new, esz) || !aligned(v_new, esz))
+    return fail(MQA_ERR_INVALID, "misaligned k_new or v_new");
+  return decode_common(q, q_dtype, out, k_new, v_new,
+                       kv_dtype == MQA_BF16 ? NewKV::kBf16 : NewKV::kF32, pool, block_table,
+                       max_pages_per_seq, context_lens, max_context, batch, num_q_heads,
+                       num_layers, num_slots, layer_slot, layer_window, softmax_scale, workspace,
+                       workspace_bytes, stream, "mqa_decode_step launch");
 }
 
 int mqa_append_attn(const void* q, mqa_dtype q_dtype, float* out, const mqa_kv_pool* pool,

@@ -15,22 +15,27 @@
 //  * One wavefront carries up to 32 query rows that read the same keys (all
 //    heads of a layer: multi-query attention means every head scores against
 //    the one KV head, so K/V are read once for all of them).
-//  * Keys are processed two pages (32 keys) at a time.  Page bytes arrive
-//    with one 16-byte load per lane per 1 KiB (layout.hpp) and are turned
-//    into exact fp16 integers in registers.
-//  * S^T = K.Q^T and O^T += V^T.P^T run on 16x16x32 fp16 matrix cores with
-//    fp32 accumulation.  The S^T tile a lane receives (4 keys of one row) is
-//    exactly the P^T operand it needs, so the softmax stays in registers.
-//  * q is scaled per row by a power of two so that its largest element lies
-//    in [2^14, 2^15): bf16 q is then exact in fp16; fp32 q is split into two
-//    fp16 terms.  P*sV is scaled by a power of two tied to the largest V scale
-//    seen so far, so the fp16 P operand keeps full precision.  The int8
-//    codes, the products and the fp32 sums make the only roundings the fp16
-//    P operand (relative 2^-11) and fp32 accumulation.
-//  * Online softmax in the log2 domain (v_exp_f32), with max and sum per row.
+//  * Keys are processed two pages (32 keys) at a time.  Every matrix-core
+//    operand is one contiguous 16-byte lane load of a page record
+//    (layout.hpp); decode streams pages HBM -> LDS with gfx950's direct
+//    global -> LDS loads.
+//  * S^T = K.Q^T runs on the int8 matrix cores (16x16x64, exact int32): the K
+//    codes are used as stored, and each q row is scaled by a power of two to
+//    a 15-bit fixed-point integer split into two int8 halves.  O^T += V^T.P^T
+//    runs on fp16 matrix cores (16x16x32, fp32 accumulate) with the V codes
+//    converted exactly to fp16.  The S^T tile a lane receives (4 keys of one
+//    row) is exactly the P^T operand it needs, so the softmax stays in
+//    registers.
+//  * P*sV is scaled by a power of two tied to the largest V scale seen so
+//    far, so the fp16 P operand keeps full precision.  The remaining
+//    roundings are the fp16 P operand (relative 2^-11), q's fixed point
+//    (elements below 2^-7 of their row's maximum) and fp32 sums.
+//  * Online softmax in the log2 domain (v_exp_f32) with a lazily moved
+//    reference maximum per row.
 //  * Decode splits long contexts into chunks (flash-decoding style): the
 //    wavefronts of a workgroup take consecutive pages and are merged through
-//    LDS; chunks of one sequence are merged by merge_kernel.
+//    LDS; the chunks of one sequence publish partial records and the last one
+//    to arrive merges them, inside the same kernel.
 #include "internal.hpp"
 
 namespace mqa {
@@ -450,11 +455,10 @@ __device__ __forceinline__ void lds_page(PageRegs<D>& r, const uint8_t* lds_slot
   r.sv = *reinterpret_cast<const f32x4*>(lds_slot + 32 * D + 64 + lg * 16);
 }
 
-// Decode workgroup LDS, as separate objects so that the compiler can tell the
-// page rings (written by global -> LDS loads) from everything else: q
-// operands converted once for all wavefronts, per-row softmax scales, the
-// wavefronts' softmax statistics, and each wavefront's 4-page ring, which the
-// final merge reuses once every page has been consumed.
+// Decode workgroup LDS: q operands converted once for all wavefronts, per-row
+// softmax scales, the wavefronts' softmax statistics and the cross-workgroup
+// arrival flag, kept apart from the page rings (written by global -> LDS
+// loads) so that the compiler can tell them apart.
 template <int D, int QS, int NRT, int W>
 struct DecodeQLds {
   static constexpr int KS8 = D / 64;
@@ -462,18 +466,22 @@ struct DecodeQLds {
   float crow[32];
   float m[W][32];
   float l[W][32];
+  int ev[W];
+  int last;
 };
-template <int D, int NRT, int W, int RB>
-union DecodeRingLds {
-  uint8_t ring[W][2 * RB][lds_slot_bytes<D>()];  // RB blocks of two pages per wavefront
-  f32x4 acc[W / 2][NRT][Geo<D>::VT][64];
+// Each wavefront's ring of RB blocks of two pages.  Once its pages are
+// consumed, a wavefront dumps its accumulators into its own ring for the
+// cross-wavefront merge.
+template <int D, int W, int RB>
+struct alignas(16) DecodeRingLds {
+  uint8_t ring[W][2 * RB][lds_slot_bytes<D>()];
 };
 
 // s_waitcnt immediate for "at most n vector-memory operations outstanding"
 // (expcnt and lgkmcnt left at their maxima; vmcnt's 6 bits are split 4 + 2).
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
 
-// The block's query rows staged into fp16 matrix-core operands in LDS, once
+// The block's query rows staged into int8 matrix-core operands in LDS, once
 // for all W wavefronts: wavefront w takes rows 4w..4w+3, 4w+4W.., 16 lanes per
 // row, D/16 channels per lane.  Loads first (StageQ::load), conversion later
 // (StageQ::store) so that other memory traffic can be issued in between.
@@ -577,17 +585,90 @@ struct StageQ {
   }
 };
 
-template <int D, int QS, int NRT, int W, int RB>
-__global__ __launch_bounds__(W * 64) void decode_kernel(
+// The current token of a fused decode step ("Como funciona a inferência de
+// IA", section "Por que o cache KV existe": a new token's K and V are computed
+// once and kept).  Its K and V rows are loaded when the workgroup starts,
+// coded to int8 with the pack kernel's arithmetic, written into the LDS copy
+// of their page before that page is read (the step never reads the token back
+// from HBM) and, by one workgroup per slot, into the pool for later steps.
+template <int D, NewKV NK>
+struct CurrentToken {
+  static constexpr int PER = D / 64;  // channels lane*PER .. lane*PER+PER-1
+  float xk[PER], xv[PER];
+  int ck[PER], cv[PER];
+  float sk, sv;
+
+  __device__ __forceinline__ void load(const void* __restrict__ kp, const void* __restrict__ vp,
+                                       int64_t row, int lane) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int64_t i = row * D + lane * PER + e;
+      if constexpr (NK == NewKV::kBf16) {
+        xk[e] = bf16_to_f32(static_cast<const uint16_t*>(kp)[i]);
+        xv[e] = bf16_to_f32(static_cast<const uint16_t*>(vp)[i]);
+      } else {
+        xk[e] = static_cast<const float*>(kp)[i];
+        xv[e] = static_cast<const float*>(vp)[i];
+      }
+    }
+  }
+  __device__ __forceinline__ void code() {
+    const float ak = wave_absmax<PER>(xk), av = wave_absmax<PER>(xv);
+    sk = quant_scale(ak);
+    sv = quant_scale(av);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      ck[e] = quant_code(xk[e], ak, sk);
+      cv[e] = quant_code(xv[e], av, sv);
+    }
+  }
+  // write the token into a page record (an LDS copy or the pool) as token j
+  __device__ __forceinline__ void put(uint8_t* rec, int j, int lane) const {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int c = lane * PER + e;
+      rec[k_code_offset(D, j, c)] = (uint8_t)ck[e];
+      rec[v_code_offset(D, j, c)] = (uint8_t)cv[e];
+    }
+    if (lane == 0) {
+      *reinterpret_cast<float*>(rec + k_scale_offset(D, j)) = sk;
+      *reinterpret_cast<float*>(rec + v_scale_offset(D, j)) = sv;
+    }
+  }
+};
+
+// Device-coherent handoff between workgroups.  Agent-scope relaxed atomic
+// loads and stores are coherent across the XCDs' separate L2 caches (gfx950
+// marks them sc1); pairing them with a wait for the stores' completion before
+// the arrival is counted avoids a full L2 write-back fence.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Decode, optionally fused with storing the current token (NK != kNone).
+// Per workgroup: stage q; stream this wavefront's pages HBM -> LDS through its
+// ring; attend; merge the W wavefronts in one LDS exchange; then either write
+// the output (the workgroup covered the whole key range) or publish a partial
+// record, count the arrival, and let the chunk that arrives last fold every
+// chunk's record in chunk order and write the output.
+template <int D, int QS, int NRT, NewKV NK>
+__global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(
     const DecodeArgs a, const void* __restrict__ qp, float* __restrict__ out,
-    const uint8_t* __restrict__ pool, const int32_t* __restrict__ block_table,
-    const int32_t* __restrict__ context_lens, float* __restrict__ ws) {
+    uint8_t* __restrict__ pool, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ context_lens, float* __restrict__ ws,
+    const void* __restrict__ k_new, const void* __restrict__ v_new) {
+  constexpr int W = kDecodeWaves, RB = kDecodeRing;
   constexpr int VT = Geo<D>::VT;
-  constexpr int KS = Geo<D>::KSTEPS;
+  constexpr int PAIRS = NRT * VT;             // (row tile, channel tile) pairs of the output
+  constexpr int PPW = (PAIRS + W - 1) / W;    // pairs per wavefront in the merge
   __shared__ DecodeQLds<D, QS, NRT, W> sm;
-  __shared__ DecodeRingLds<D, NRT, W, RB> ring;
-  static_assert(sizeof(DecodeQLds<D, QS, NRT, W>) + sizeof(DecodeRingLds<D, NRT, W, RB>) <= 160 * 1024,
+  __shared__ DecodeRingLds<D, W, RB> ring;
+  static_assert(sizeof(DecodeQLds<D, QS, NRT, W>) + sizeof(DecodeRingLds<D, W, RB>) <= 160 * 1024,
                 "LDS");
+  static_assert(PAIRS * 64 * sizeof(f32x4) <= sizeof(ring.ring[0]), "accumulator dump");
   constexpr int DMA_PER_BLOCK = 2 * (32 * D / 1024 + 1);
   const int w = swizzled_block();
   if (w >= a.total_wgs) return;
@@ -603,7 +684,7 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(
   decode_range(ctx, g.window, lo, hi);
   const int64_t out_row0 = ((int64_t)rb.layer * a.batch + seq) * a.num_q_heads + rb.head0;
 
-  if (hi <= lo) {  // empty context: zeros
+  if (hi <= lo) {  // empty context: zeros (and no current token to store)
     if (chunk == 0 && wv == 0) {
       for (int n = 0; n < NRT; ++n) {
         const int row = 16 * n + li;
@@ -620,9 +701,9 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(
   const int nch = (p_last - p_first + ppc) / ppc;
   if (chunk >= nch) return;
 
-  // Memory traffic in this order: the query rows and this wavefront's page
-  // ids together, then the first page pair straight into LDS; q is converted
-  // while the pages are in flight.
+  // Memory traffic in this order: the query rows, this wavefront's page ids
+  // and the current token's rows together, then the first page pair straight
+  // into LDS; q is converted while the pages are in flight.
   StageQ<D, QS, NRT, W> sq;
   sq.load(static_cast<const uint8_t*>(qp) + out_row0 * D * (QS == 1 ? 2 : 4), rb.nrows, wv, lane);
   const int pbeg = p_first + chunk * ppc + wv * g.pages_per_wave;
@@ -633,6 +714,9 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(
     pid = __builtin_amdgcn_readlane(ids, min(max(pi - pbeg, 0), 63));
     return pi < pend && (uint32_t)pid < (uint64_t)a.num_pages;
   };
+  CurrentToken<D, NK> cur;
+  if constexpr (NK != NewKV::kNone)
+    cur.load(k_new, v_new, (int64_t)g.slot * a.batch + seq, lane);
   // branch-free: a page that is out of range or has a bad id loads page 0
   // instead (it exists) and is masked later
   auto issue_block = [&](int pa, int slot0) {
@@ -651,6 +735,7 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(
   for (int i = 0; i < RB - 1; ++i) issue_block(pbeg + 2 * i, 2 * i);
   __builtin_amdgcn_sched_barrier(0);
   sq.store(sm, rb.nrows, a.scale_log2, wv, lane);
+  if constexpr (NK != NewKV::kNone) cur.code();
   __syncthreads();
   QOps<D, QS, NRT> q;
 #pragma unroll
@@ -662,19 +747,24 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(
       for (int h = 0; h < D / 64; ++h) q.q8[n][hl][h] = sm.q8[n][hl][h][lane];
   }
 
+  const int tok = (hi - 1) & 15;  // the current token's place in page p_last
   WaveState<D, NRT> st;
   st.init();
   for (int b = 0; b < nblk; ++b) {
     const int pa = pbeg + 2 * b;
-    const int cur = 2 * (b % RB);
+    const int cs = 2 * (b % RB);
     // The compiler does not track global -> LDS loads: wait for them here.
     // In flight are blocks b .. b+RB-2 (issued in order): leave the younger
     // ones outstanding.
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((RB - 2) * DMA_PER_BLOCK));
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NK != NewKV::kNone) {
+      if (pa == p_last || pa + 1 == p_last)  // wave-uniform
+        cur.put(ring.ring[wv][cs + (p_last - pa)], tok, lane);
+    }
     PageRegs<D> c0, c1;
-    lds_page<D>(c0, ring.ring[wv][cur], lane, lg);
-    lds_page<D>(c1, ring.ring[wv][cur + 1], lane, lg);
+    lds_page<D>(c0, ring.ring[wv][cs], lane, lg);
+    lds_page<D>(c1, ring.ring[wv][cs + 1], lane, lg);
     int pid0, pid1;
     const bool ok0 = page_ok(pa, pid0), ok1 = page_ok(pa + 1, pid1);
     // block b+RB-1 into the slots read one iteration ago; flies during compute.
@@ -683,11 +773,19 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(
     if (RB > 2 || b + 1 < nblk) issue_block(pa + 2 * (RB - 1), 2 * ((b + RB - 1) % RB));
     attend_block_any<D, QS, NRT>(st, q, c0, c1, ok0, ok1, pa * kPageTokens, lo, hi, lg);
   }
+  if constexpr (NK != NewKV::kNone) {
+    // one workgroup per slot and sequence keeps the token for later steps
+    if (g.writes_new_kv && dw.rbl == 0 && p_last >= pbeg && p_last < pend) {
+      int pid;
+      if (page_ok(p_last, pid)) cur.put(pool + (int64_t)pid * page_bytes(D), tok, lane);
+    }
+  }
 
-  // ---- merge the W wavefronts of the workgroup through LDS (pairwise tree) ----
-  // Every page load into this wavefront's ring has landed before the rings
-  // are reused below.
+  // ---- merge the W wavefronts: one LDS exchange ----
+  // Every page load into this wavefront's ring has landed, so the wavefront
+  // can dump its accumulators into its own ring without waiting for others.
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  f32x4* dump = reinterpret_cast<f32x4*>(&ring.ring[wv][0][0]);
 #pragma unroll
   for (int n = 0; n < NRT; ++n) {
     const float lrow = row_sum4(st.l[n]);
@@ -695,135 +793,139 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(
       sm.m[wv][16 * n + li] = st.m[n];
       sm.l[wv][16 * n + li] = lrow;
     }
-  }
-  __syncthreads();  // also: every wavefront is done with its ring
-  float M[NRT], L[NRT];
 #pragma unroll
-  for (int n = 0; n < NRT; ++n) {
-    const int row = 16 * n + li;
+    for (int t = 0; t < VT; ++t) dump[(n * VT + t) * 64 + lane] = st.acc[n][t];
+  }
+  if (lane == 0) sm.ev[wv] = st.ev;
+  __syncthreads();
+  // Wavefront wv merges output pairs wv, wv+W, ...: row 16n+li, channels
+  // 16t+4lg .. +3.  Each wavefront's accumulators are relative to 2^m (its
+  // running max) and carry P*sV scaled by 2^(kPvBias-ev).
+  float Mr[PPW], Lr[PPW];
+  f32x4 Ar[PPW];
+#pragma unroll
+  for (int k = 0; k < PPW; ++k) {
+    const int pi = wv + k * W;
+    Mr[k] = kNegInf;
+    Lr[k] = 0.0f;
+    Ar[k] = f32x4{0, 0, 0, 0};
+    if (pi >= PAIRS) continue;  // wave-uniform
+    const int row = 16 * (pi / VT) + li;
     float mm = kNegInf;
 #pragma unroll
     for (int x = 0; x < W; ++x) mm = fmaxf(mm, sm.m[x][row]);
     const float mu = mm == kNegInf ? 0.0f : mm;
     float ll = 0.0f;
+    f32x4 acc = f32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int x = 0; x < W; ++x) ll += fast_exp2(sm.m[x][row] - mu) * sm.l[x][row];
-    M[n] = mm;
-    L[n] = ll;
-    const float fac = st.ev == kNoExp ? 0.0f : ldexp2(fast_exp2(st.m[n] - mu), st.ev - kPvBias);
-#pragma unroll
-    for (int t = 0; t < VT; ++t) st.acc[n][t] *= fac;
-  }
-#pragma unroll
-  for (int half = W / 2; half >= 1; half >>= 1) {
-    if (wv >= half && wv < 2 * half) {
-#pragma unroll
-      for (int n = 0; n < NRT; ++n)
-#pragma unroll
-        for (int t = 0; t < VT; ++t) ring.acc[wv - half][n][t][lane] = st.acc[n][t];
+    for (int x = 0; x < W; ++x) {
+      const float e = fast_exp2(sm.m[x][row] - mu);
+      ll += e * sm.l[x][row];
+      const int evx = sm.ev[x];
+      const float f = evx == kNoExp ? 0.0f : ldexp2(e, evx - kPvBias);
+      acc += f * reinterpret_cast<const f32x4*>(&ring.ring[x][0][0])[pi * 64 + lane];
     }
-    __syncthreads();
-    if (wv < half) {
-#pragma unroll
-      for (int n = 0; n < NRT; ++n)
-#pragma unroll
-        for (int t = 0; t < VT; ++t) st.acc[n][t] += ring.acc[wv][n][t][lane];
-    }
-    if (half > 1) __syncthreads();
+    Mr[k] = mm;
+    Lr[k] = ll;
+    Ar[k] = acc;
   }
-  if (wv != 0) return;
 
   if (nch == 1) {  // the workgroup saw the whole range: write the output
 #pragma unroll
-    for (int n = 0; n < NRT; ++n) {
-      const int row = 16 * n + li;
+    for (int k = 0; k < PPW; ++k) {
+      const int pi = wv + k * W;
+      if (pi >= PAIRS) continue;
+      const int row = 16 * (pi / VT) + li, t = pi % VT;
       if (row >= rb.nrows) continue;
-      const float inv = L[n] > 0.0f ? 1.0f / L[n] : 0.0f;
-      float* o = out + (out_row0 + row) * D + 4 * lg;
-#pragma unroll
-      for (int t = 0; t < VT; ++t) *reinterpret_cast<f32x4*>(o + 16 * t) = st.acc[n][t] * inv;
+      const float inv = Lr[k] > 0.0f ? 1.0f / Lr[k] : 0.0f;
+      *reinterpret_cast<f32x4*>(out + (out_row0 + row) * D + 16 * t + 4 * lg) = Ar[k] * inv;
     }
     return;
   }
-  // several chunks: write this chunk's partial record for merge_kernel
-  float* rec = ws + ((int64_t)g.ws_begin + ((int64_t)dw.rbl * a.batch + seq) * g.nchunk + chunk) *
-                        ws_record_floats(D);
-#pragma unroll
-  for (int n = 0; n < NRT; ++n) {
-    const int row = 16 * n + li;
-    if (lg == 0) {
-      rec[row] = M[n];
-      rec[32 + row] = L[n];
-    }
-    float* o = rec + 64 + row * D + 4 * lg;
-#pragma unroll
-    for (int t = 0; t < VT; ++t) *reinterpret_cast<f32x4*>(o + 16 * t) = st.acc[n][t];
-  }
-}
 
-// ---------------------------------------------------------------------------
-// Decode merge: one workgroup = 8 rows of one (row block, sequence); thread t
-// takes row t/32 of them and D/32 consecutive channels.  Partial records:
-// m[32], l[32], acc[32][D] (acc and l relative to exp2(m)).
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a,
-                                                    const int32_t* __restrict__ context_lens,
-                                                    const float* __restrict__ ws,
-                                                    float* __restrict__ out) {
-  int w = blockIdx.x >> 2;
-  const int quarter = blockIdx.x & 3;
-  int gi = 0;
-  while (gi < a.num_groups && w >= a.groups[gi].num_rb * a.batch) {
-    w -= a.groups[gi].num_rb * a.batch;
-    ++gi;
-  }
-  if (gi >= a.num_groups) return;
-  const DecodeGroup& g = a.groups[gi];
-  if (g.nchunk <= 1) return;
-  const int rbl = w / a.batch, seq = w % a.batch;
-  const RowBlock& rb = a.rbs[g.first_rb + rbl];
-  const int ctx = clamp_ctx(context_lens[seq], a.max_context, a.max_pages);
-  int lo, hi;
-  decode_range(ctx, g.window, lo, hi);
-  if (hi <= lo) return;
-  const int ppc = g.pages_per_wave * g.waves;
-  const int nch = ((hi - 1) / 16 - lo / 16 + ppc) / ppc;
-  if (nch <= 1) return;
-  const int row = quarter * 8 + (threadIdx.x >> 5), part = threadIdx.x & 31;
-  if (row >= rb.nrows) return;
-  constexpr int PER = D / 32;
+  // ---- several chunks: publish this chunk's partial record ----
   constexpr int64_t RS = ws_record_floats(D);
-  const float* rec0 =
-      ws + ((int64_t)g.ws_begin + ((int64_t)rbl * a.batch + seq) * g.nchunk) * RS;
-  float mm = kNegInf;
-#pragma unroll 8
-  for (int c = 0; c < nch; ++c) mm = fmaxf(mm, rec0[c * RS + row]);
-  const float mu = mm == kNegInf ? 0.0f : mm;
-  float acc[PER];
+  const int64_t rec0 = (int64_t)g.ws_begin + ((int64_t)dw.rbl * a.batch + seq) * g.nchunk;
+  float* const recs = ws + kDecodeCounters;
+  float* mine = recs + (rec0 + chunk) * RS;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
-  float ll = 0.0f;
-#pragma unroll 8
-  for (int c = 0; c < nch; ++c) {
-    const float* rec = rec0 + c * RS;
-    const float f = fast_exp2(rec[row] - mu);
-    ll += f * rec[32 + row];
-    const float* src = rec + 64 + row * D + part * PER;
-    if constexpr (PER == 4) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(src);
+  for (int k = 0; k < PPW; ++k) {
+    const int pi = wv + k * W;
+    if (pi >= PAIRS) continue;
+    const int row = 16 * (pi / VT) + li;
+    if (pi % VT == 0 && lg == 0) {
+      st_dev(mine + row, Mr[k]);
+      st_dev(mine + 32 + row, Lr[k]);
+    }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] += f * x[e];
-    } else {
+    for (int e = 0; e < 4; ++e) st_dev(mine + 64 + (pi * 4 + e) * 64 + lane, Ar[k][e]);
+  }
+  // every wavefront's stores have completed before the arrival is counted
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(ws) + g.merge_begin + (int64_t)dw.rbl * a.batch +
+                    seq;
+    const uint32_t before = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+    const int last = before == (uint32_t)(nch - 1);
+    // the last arrival leaves the counter at zero for the next call
+    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm.last = last;
+  }
+  __syncthreads();
+  if (!sm.last) return;
+
+  // ---- the last chunk to arrive: fold all records in chunk order ----
+  // (the order, not the arrival, fixes the rounding: results are deterministic)
+  constexpr int CB = 8;  // records loaded per round trip
+  float M[PPW], L[PPW];
+  f32x4 A[PPW];
 #pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] += f * src[e];
+  for (int k = 0; k < PPW; ++k) {
+    M[k] = kNegInf;
+    L[k] = 0.0f;
+    A[k] = f32x4{0, 0, 0, 0};
+  }
+  for (int c0 = 0; c0 < nch; c0 += CB) {
+    float mc[PPW][CB], lc[PPW][CB];
+    f32x4 ac[PPW][CB];
+#pragma unroll
+    for (int k = 0; k < PPW; ++k) {
+      const int pi = min(wv + k * W, PAIRS - 1);
+      const int row = 16 * (pi / VT) + li;
+#pragma unroll
+      for (int u = 0; u < CB; ++u) {
+        const float* r = recs + (rec0 + min(c0 + u, nch - 1)) * RS;
+        mc[k][u] = ld_dev(r + row);
+        lc[k][u] = ld_dev(r + 32 + row);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ac[k][u][e] = ld_dev(r + 64 + (pi * 4 + e) * 64 + lane);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      if (c0 + u >= nch) break;
+#pragma unroll
+      for (int k = 0; k < PPW; ++k) {
+        const float mn = fmaxf(M[k], mc[k][u]);
+        const float mu = mn == kNegInf ? 0.0f : mn;
+        const float fa = fast_exp2(M[k] - mu), fb = fast_exp2(mc[k][u] - mu);
+        L[k] = L[k] * fa + lc[k][u] * fb;
+        A[k] = A[k] * fa + ac[k][u] * fb;
+        M[k] = mn;
+      }
     }
   }
-  const float inv = ll > 0.0f ? 1.0f / ll : 0.0f;
-  float* o = out + (((int64_t)rb.layer * a.batch + seq) * a.num_q_heads + rb.head0 + row) * D +
-             part * PER;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) o[e] = acc[e] * inv;
+  for (int k = 0; k < PPW; ++k) {
+    const int pi = wv + k * W;
+    if (pi >= PAIRS) continue;
+    const int row = 16 * (pi / VT) + li, t = pi % VT;
+    if (row >= rb.nrows) continue;
+    const float inv = L[k] > 0.0f ? 1.0f / L[k] : 0.0f;
+    *reinterpret_cast<f32x4*>(out + (out_row0 + row) * D + 16 * t + 4 * lg) = A[k] * inv;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -913,31 +1015,25 @@ __global__ __launch_bounds__(kAttnWaves * 64) void append_kernel(
 // ---------------------------------------------------------------------------
 static inline dim3 padded_grid(int total) { return dim3((unsigned)((total + 7) / 8 * 8)); }
 
-template <int D, int QS, int NRT, int W, int RB>
-static hipError_t launch_decode_t(const DecodeArgs& a, const DecodePtrs& p, bool need_merge,
-                                  hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<D, QS, NRT, W, RB>), padded_grid(a.total_wgs), dim3(W * 64), 0,
-                     stream, a, p.q, p.out, p.pool, p.block_table, p.context_lens, p.ws);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !need_merge) return e;
-  hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)a.total_merge * 4), dim3(256), 0, stream,
-                     a, p.context_lens, p.ws, p.out);
+template <int D, int QS, int NRT, NewKV NK>
+static hipError_t launch_decode_t(const DecodeArgs& a, const DecodePtrs& p, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_kernel<D, QS, NRT, NK>), padded_grid(a.total_wgs),
+                     dim3(kDecodeWaves * 64), 0, stream, a, p.q, p.out, p.pool, p.block_table,
+                     p.context_lens, p.ws, p.k_new, p.v_new);
   return hipGetLastError();
 }
 
-// waves x ring depth: (8, 2), (4, 2), (4, 3), (4, 4) -- each fits the 160 KiB LDS
 template <int D, int QS, int NRT>
-static hipError_t launch_decode_w(int waves, int ring, const DecodeArgs& a, const DecodePtrs& p,
-                                  bool need_merge, hipStream_t stream) {
-  if (waves == 8) return launch_decode_t<D, QS, NRT, 8, 2>(a, p, need_merge, stream);
-  if (ring == 4) return launch_decode_t<D, QS, NRT, 4, 4>(a, p, need_merge, stream);
-  if (ring == 3) return launch_decode_t<D, QS, NRT, 4, 3>(a, p, need_merge, stream);
-  return launch_decode_t<D, QS, NRT, 4, 2>(a, p, need_merge, stream);
+static hipError_t launch_decode_n(NewKV nk, const DecodeArgs& a, const DecodePtrs& p,
+                                  hipStream_t stream) {
+  if (nk == NewKV::kBf16) return launch_decode_t<D, QS, NRT, NewKV::kBf16>(a, p, stream);
+  if (nk == NewKV::kF32) return launch_decode_t<D, QS, NRT, NewKV::kF32>(a, p, stream);
+  return launch_decode_t<D, QS, NRT, NewKV::kNone>(a, p, stream);
 }
 
-hipError_t launch_decode(int D, bool q_f32, int nrt, int waves, int ring, const DecodeArgs& a,
-                         const DecodePtrs& p, bool need_merge, hipStream_t stream) {
-#define MQA_DEC(DD, QQ, NN) return launch_decode_w<DD, QQ, NN>(waves, ring, a, p, need_merge, stream)
+hipError_t launch_decode(int D, bool q_f32, int nrt, NewKV nk, const DecodeArgs& a,
+                         const DecodePtrs& p, hipStream_t stream) {
+#define MQA_DEC(DD, QQ, NN) return launch_decode_n<DD, QQ, NN>(nk, a, p, stream)
   if (D == 128) {
     if (q_f32) { if (nrt == 1) MQA_DEC(128, 2, 1); MQA_DEC(128, 2, 2); }
     if (nrt == 1) MQA_DEC(128, 1, 1);

@@ -115,4 +115,28 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return bitcast<float>((uint32_t)b << 16);
 }
 
+// ---------------------------------------------------------------------------
+// Symmetric int8 coding of one K or V row with one fp32 scale
+// ("Character.AI: inference optimization", section 05: the KV cache is int8):
+//   a = max|x|,  s = a / 127 (fp32),  code = clamp(rint(x / s), -127, 127)
+// with IEEE fp32 division (hipcc's default `/` is correctly rounded) and
+// round-half-to-even; a = 0 gives s = 0 and zero codes.
+// ---------------------------------------------------------------------------
+// max |x| over a wavefront's PER values per lane; every lane gets the result
+template <int PER>
+__device__ __forceinline__ float wave_absmax(const float (&x)[PER]) {
+  float a = 0.0f;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) a = fmaxf(a, fabsf(x[e]));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
+  return a;
+}
+__device__ __forceinline__ float quant_scale(float a) { return a / 127.0f; }
+__device__ __forceinline__ int quant_code(float x, float a, float s) {
+  if (a == 0.0f) return 0;
+  const float r = __builtin_rintf(x / s);
+  return (int)fminf(fmaxf(r, -127.0f), 127.0f);
+}
+
 }  // namespace mqa

@@ -32,8 +32,8 @@ struct DecodeGroup {
   int32_t nchunk;          // chunks per sequence planned for max_context
   int32_t wg_begin;        // first flat workgroup of the group
   int32_t ws_begin;        // first workspace record of the group
-  int32_t merge_begin;     // first merge workgroup of the group (row blocks x batch before it)
-  int32_t waves;           // wavefronts per decode workgroup
+  int32_t merge_begin;     // first arrival counter of the group (row blocks x batch before it)
+  int32_t writes_new_kv;   // this group stores the slot's current token (first group of a slot)
 };
 
 struct DecodeArgs {
@@ -44,7 +44,7 @@ struct DecodeArgs {
   int32_t num_q_heads;
   int32_t num_groups;
   int32_t total_wgs;
-  int32_t total_merge;  // row blocks x batch
+  int32_t total_merge;  // row blocks x batch (one arrival counter each)
   float scale_log2;     // softmax scale * log2(e)
   DecodeGroup groups[kMaxGroups];
   RowBlock rbs[kMaxRowBlocks];
@@ -55,11 +55,16 @@ struct DecodeArgs {
 struct DecodePtrs {
   const void* q;
   float* out;
-  const uint8_t* pool;
+  uint8_t* pool;
   const int32_t* block_table;
   const int32_t* context_lens;
-  float* ws;            // partial records of sequences split into several chunks
+  float* ws;            // partial records + arrival counters (split sequences only)
+  const void* k_new;    // current token's K rows [num_slots][batch][D] (fused step) or null
+  const void* v_new;
 };
+
+// The current token's K/V handed to the fused decode step.
+enum class NewKV { kNone = 0, kBf16 = 1, kF32 = 2 };
 
 struct AppendArgs {
   int64_t num_pages;
@@ -92,13 +97,22 @@ hipError_t launch_pack(int D, bool bf16, const void* k, const void* v, int64_t n
                        int64_t row_stride, const int64_t* slot_mapping, uint8_t* pool,
                        int64_t num_pages, hipStream_t stream);
 
-hipError_t launch_decode(int D, bool q_f32, int nrt, int waves, int ring, const DecodeArgs& a,
-                         const DecodePtrs& p, bool need_merge, hipStream_t stream);
+hipError_t launch_decode(int D, bool q_f32, int nrt, NewKV new_kv, const DecodeArgs& a,
+                         const DecodePtrs& p, hipStream_t stream);
 
 hipError_t launch_append(int D, bool q_f32, int nrt, const AppendArgs& a, const AppendPtrs& p,
                          hipStream_t stream);
 
-// Decode workspace record: m[32], l[32], acc[32][D] fp32.
+// Decode workspace: a fixed prefix of 32-bit arrival counters, one per
+// (row block, sequence) of a call, then one partial record per (row block,
+// sequence, chunk) of a split sequence -- m[32], l[32] and acc[32 * D] fp32,
+// acc in matrix-core operand order ((16-row tile, 16-channel tile, element) x
+// 64 lanes).  The counter prefix has the same size and place for every call
+// shape, so calls of different shapes can share one workspace: each leaves
+// its counters at zero and records never overwrite a counter.
 constexpr int64_t ws_record_floats(int D) { return kRowsPerBlock * (D + 2); }
+constexpr int64_t kDecodeCounters = 65536;  // 256 KiB
+constexpr int kDecodeWaves = 8;     // wavefronts per decode workgroup
+constexpr int kDecodeRing = 2;      // blocks of two pages in flight per wavefront
 
 }  // namespace mqa

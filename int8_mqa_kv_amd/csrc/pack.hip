@@ -3,11 +3,10 @@
 //
 // The cache is int8 ("Character.AI: inference optimization", section 05) and
 // K/V of a new token are computed once and kept ("Como funciona a inferência
-// de IA", section "Por que o cache KV existe").  Code of a row x:
-//   a = max|x|,  s = a / 127 (fp32),  code = clamp(rint(x / s), -127, 127)
-// with IEEE fp32 division and round-half-to-even; a = 0 gives s = 0 and zero
-// codes.  The division is the correctly rounded one (no reciprocal multiply,
-// no fast-math), so the bytes match that definition exactly.
+// de IA", section "Por que o cache KV existe").  The coding of a row
+// (wave_absmax, quant_scale, quant_code in device.hpp) is shared with the
+// fused decode step, which codes the current token the same way, so both
+// write the same bytes.
 #include "internal.hpp"
 
 namespace mqa {
@@ -43,26 +42,15 @@ __global__ __launch_bounds__(kPackWaves * 64) void pack_kernel(
   for (int which = 0; which < 2; ++which) {
     const void* src = which == 0 ? k : v;
     float x[PER];
-    float a = 0.0f;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      x[e] = load_elem<D, BF16>(src, t * row_stride + lane * PER + e);
-      a = fmaxf(a, fabsf(x[e]));
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
-    const float s = a / 127.0f;
+    for (int e = 0; e < PER; ++e) x[e] = load_elem<D, BF16>(src, t * row_stride + lane * PER + e);
+    const float a = wave_absmax<PER>(x);
+    const float s = quant_scale(a);
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
       const int c = lane * PER + e;
-      int code = 0;
-      if (a != 0.0f) {
-        float r = __builtin_rintf(x[e] / s);
-        r = fminf(fmaxf(r, -127.0f), 127.0f);
-        code = (int)r;
-      }
       const int off = which == 0 ? k_code_offset(D, j, c) : v_code_offset(D, j, c);
-      rec[off] = (uint8_t)(int8_t)code;
+      rec[off] = (uint8_t)(int8_t)quant_code(x[e], a, s);
     }
     if (lane == 0) {
       const int off = which == 0 ? k_scale_offset(D, j) : v_scale_offset(D, j);
