@@ -116,18 +116,6 @@ int target_workgroups() {
   return v;
 }
 
-// MQA_DECODE_PAGES_PER_WAVE fixes the pages each wavefront takes (even, at
-// most 64), another tuning aid; 0 lets the planner choose.
-int forced_pages_per_wave() {
-  static const int v = [] {
-    const char* e = getenv("MQA_DECODE_PAGES_PER_WAVE");
-    int t = e ? atoi(e) : 0;
-    if (t > 0 && (t & 1)) ++t;
-    return std::min(t, 64);
-  }();
-  return v;
-}
-
 DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
                        const int32_t* layer_slot, const int32_t* layer_window,
                        int32_t max_context, int32_t head_dim) {
@@ -161,20 +149,30 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
     return p;
   }
 
-  // pages a sequence can span in each group, and the total page work
+  // Pages a sequence can span in each group (a window that does not start on
+  // a page boundary touches one page more), and the work of all items, an
+  // item being one row block of one sequence.
+  const int64_t ctx_pages = (max_context + kPageTokens - 1) / kPageTokens;
   std::vector<int64_t> max_np(keys.size());
-  int64_t total_pages = 0;
+  int64_t items = 0, work = 0;
   for (size_t g = 0; g < keys.size(); ++g) {
     const int w = keys[g].second;
-    const int64_t span = w > 0 ? std::min<int64_t>(w, max_context) : max_context;
-    max_np[g] = (span + kPageTokens - 1) / kPageTokens + 1;
-    total_pages += max_np[g] * (int64_t)members[g].size() * head_blocks * batch;
+    max_np[g] = w > 0 ? std::min<int64_t>((w + kPageTokens - 1) / kPageTokens + 1, ctx_pages)
+                      : ctx_pages;
+    const int64_t n = (int64_t)members[g].size() * head_blocks * batch;
+    items += n;
+    work += n * max_np[g];
   }
-  int ppw = forced_pages_per_wave();
-  if (ppw <= 0) {
-    const double x = (double)total_pages / ((double)target_workgroups() * kDecodeWaves);
-    ppw = std::max(2, 2 * (int)llround(x / 2.0));
-    ppw = std::min(ppw, 64);  // one register window of page ids per wavefront
+  // Chunks per item: a share of the target workgroup count in proportion to
+  // the item's span, so that one round of workgroups covers the launch with
+  // equal work per workgroup and none left idle; at least enough chunks that
+  // no wavefront takes more than 64 pages (one register of page ids).
+  const int64_t target = std::max<int64_t>(target_workgroups(), items);
+  std::vector<int64_t> nchunk(keys.size());
+  for (size_t g = 0; g < keys.size(); ++g) {
+    const int64_t share = target * max_np[g] / std::max<int64_t>(work, 1);
+    const int64_t need = (max_np[g] + 64 * kDecodeWaves - 1) / (64 * kDecodeWaves);
+    nchunk[g] = std::max<int64_t>({1, share, need});
   }
 
   int rb = 0;
@@ -197,9 +195,7 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
         ++rb;
       }
     G.num_rb = rb - G.first_rb;
-    G.pages_per_wave = ppw;
-    const int64_t ppc = (int64_t)ppw * kDecodeWaves;
-    G.nchunk = (int)((max_np[g] + ppc - 1) / ppc);
+    G.nchunk = (int)nchunk[g];
     G.wg_begin = (int)wg;
     G.ws_begin = (int)ws;
     G.merge_begin = (int)merges;

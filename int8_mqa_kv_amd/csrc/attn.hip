@@ -253,29 +253,32 @@ __device__ __forceinline__ void attend_block(WaveState<D, NRT>& st, const QOps<D
   bool rescale = false;
 #pragma unroll
   for (int n = 0; n < NRT; ++n) {
-    float sig[2][4];
-    float mx = kNegInf;
+    // t = int score * key scale; the row's factor crow (> 0) is applied in
+    // the exponent's FMA, so the row max is taken on t
+    float t[2][4];
+    float mt = kNegInf;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float sk = (u ? p1.sk : p0.sk)[r];
-        const float x = s[n][u][r] * (sk * q.crow[n]);
-        sig[u][r] = MASKED ? (valid[u][r] ? x : kNegInf) : x;
-        mx = fmaxf(mx, sig[u][r]);
+        const float x = s[n][u][r] * (u ? p1.sk : p0.sk)[r];
+        t[u][r] = MASKED ? (valid[u][r] ? x : kNegInf) : x;
+        mt = fmaxf(mt, t[u][r]);
       }
-    mx = row_max4(mx);
+    mt = row_max4(mt);
+    const float c = q.crow[n];
+    const float mx = mt == kNegInf ? kNegInf : mt * c;
     const bool move = mx > st.m[n] + kTau;  // also true for the first valid block
     const float m_new = move ? mx : st.m[n];
     alpha[n] = move ? fast_exp2(st.m[n] - m_new) : 1.0f;  // exp2(-inf) = 0
     rescale |= move;
-    const float m_use = m_new == kNegInf ? 0.0f : m_new;
+    const float neg_m = m_new == kNegInf ? 0.0f : -m_new;
     float ps = 0.0f;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float pr = fast_exp2(sig[u][r] - m_use);
+        const float pr = fast_exp2(__builtin_fmaf(t[u][r], c, neg_m));
         ps += pr;
         const float pv = pr * ((u ? p1.sv : p0.sv)[r] * pvm);
         pop[n][4 * u + r] = (_Float16)(MASKED ? (valid[u][r] ? pv : 0.0f) : pv);
@@ -480,50 +483,67 @@ struct alignas(16) DecodeRingLds {
 // s_waitcnt immediate for "at most n vector-memory operations outstanding"
 // (expcnt and lgkmcnt left at their maxima; vmcnt's 6 bits are split 4 + 2).
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
+// s_waitcnt immediate for "no LDS operation outstanding" (vmcnt, expcnt at max).
+constexpr int kLgkmZero = 0xC07F;
+
+// Workgroup barrier that publishes this wavefront's LDS writes but leaves its
+// global -> LDS page loads in flight (__syncthreads() would wait for every
+// outstanding memory operation first).  The empty asm statements keep the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kLgkmZero);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // The block's query rows staged into int8 matrix-core operands in LDS, once
 // for all W wavefronts: wavefront w takes rows 4w..4w+3, 4w+4W.., 16 lanes per
-// row, D/16 channels per lane.  Loads first (StageQ::load), conversion later
-// (StageQ::store) so that other memory traffic can be issued in between.
+// row, D/16 channels per lane.  The raw rows travel global -> LDS first
+// (StageQ::issue, into the wavefront's own staging area): such loads are
+// issued where they stand, while ordinary loads whose results are used only
+// past the kernel's early exits would be sunk below them by the compiler.
+// StageQ::store then converts them once they have landed.
 template <int D, int QS, int NRT, int W>
 struct StageQ {
   static constexpr int PER = D / 16;                       // channels per lane
   static constexpr int PASSES = (16 * NRT + 4 * W - 1) / (4 * W);
-  static constexpr int WORDS = PER * (QS == 1 ? 2 : 4) / 4;  // dwords per lane per pass
-  uint32_t raw[PASSES][WORDS];
+  static constexpr int ESZ = QS == 1 ? 2 : 4;
+  static constexpr int LB = PER * ESZ;                     // raw bytes per lane per pass
+  static constexpr int CB = LB >= 16 ? 16 : 4;             // bytes per global -> LDS load
+  static constexpr int NC = LB / CB;                       // loads per lane per pass
+  static constexpr int STAGE_BYTES = PASSES * NC * 64 * CB;
+  static constexpr int WORDS = LB / 4;                     // dwords per lane per pass
 
-  __device__ __forceinline__ void load(const void* __restrict__ qrow0, int nrows, int wv,
-                                       int lane) {
-    constexpr int esz = QS == 1 ? 2 : 4;
+  __device__ __forceinline__ void issue(uint8_t* stage, const void* __restrict__ qrow0, int nrows,
+                                        int wv, int lane) const {
     const int sub = lane >> 4, part = lane & 15;
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
+      if (wv * 4 + ps * 4 * W >= 16 * NRT) break;  // wave-uniform: no rows to stage
       const int row = wv * 4 + ps * 4 * W + sub;
       const int rr = row < nrows ? row : 0;
-      const uint32_t* src = reinterpret_cast<const uint32_t*>(
-          static_cast<const uint8_t*>(qrow0) + ((int64_t)rr * D + part * PER) * esz);
-      if constexpr (WORDS == 4) {
-        const u32x4 w4 = *reinterpret_cast<const u32x4*>(src);
+      const uint8_t* src = static_cast<const uint8_t*>(qrow0) + ((int64_t)rr * D + part * PER) * ESZ;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) raw[ps][e] = w4[e];
-      } else if constexpr (WORDS == 2) {
-        const u32x2 w2 = *reinterpret_cast<const u32x2*>(src);
-        raw[ps][0] = w2[0];
-        raw[ps][1] = w2[1];
-      } else {
-#pragma unroll
-        for (int e = 0; e < WORDS; e += 4) {
-          const u32x4 w4 = *reinterpret_cast<const u32x4*>(src + e);
-#pragma unroll
-          for (int k = 0; k < 4; ++k) raw[ps][e + k] = w4[k];
-        }
+      for (int k = 0; k < NC; ++k) {
+        if constexpr (CB == 16)
+          __builtin_amdgcn_global_load_lds(src + k * 16, stage + (ps * NC + k) * 64 * 16, 16, 0, 0);
+        else
+          __builtin_amdgcn_global_load_lds(src + k * 4, stage + (ps * NC + k) * 64 * 4, 4, 0, 0);
       }
     }
   }
 
+  // dword w of this lane's raw row data of pass ps
+  __device__ __forceinline__ uint32_t raw(const uint8_t* stage, int ps, int w, int lane) const {
+    const int k = (4 * w) / CB;
+    return *reinterpret_cast<const uint32_t*>(stage + (ps * NC + k) * 64 * CB + lane * CB +
+                                              (4 * w) % CB);
+  }
+
   template <typename Lds>
-  __device__ __forceinline__ void store(Lds& sm, int nrows, float scale_log2, int wv,
-                                        int lane) const {
+  __device__ __forceinline__ void store(Lds& sm, const uint8_t* stage, int nrows,
+                                        float scale_log2, int wv, int lane) const {
     constexpr int CH = Geo<D>::CH;
     const int sub = lane >> 4, part = lane & 15;
 #pragma unroll
@@ -533,16 +553,19 @@ struct StageQ {
       if (wv * 4 + ps * 4 * W >= 16 * NRT) break;  // wave-uniform
       const int row = wv * 4 + ps * 4 * W + sub;
       const bool live = row < nrows;
+      uint32_t rw[WORDS];
+#pragma unroll
+      for (int e = 0; e < WORDS; ++e) rw[e] = raw(stage, ps, e, lane);
       float x[PER];
       if constexpr (QS == 1) {
 #pragma unroll
         for (int e = 0; e < PER / 2; ++e) {
-          x[2 * e] = bitcast<float>(raw[ps][e] << 16);
-          x[2 * e + 1] = bitcast<float>(raw[ps][e] & 0xffff0000u);
+          x[2 * e] = bitcast<float>(rw[e] << 16);
+          x[2 * e + 1] = bitcast<float>(rw[e] & 0xffff0000u);
         }
       } else {
 #pragma unroll
-        for (int e = 0; e < PER; ++e) x[e] = bitcast<float>(raw[ps][e]);
+        for (int e = 0; e < PER; ++e) x[e] = bitcast<float>(rw[e]);
       }
       float a = 0.0f;
 #pragma unroll
@@ -679,10 +702,17 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(
 
   const int lane = lane_id(), li = lane & 15, lg = lane >> 4;
   const int wv = threadIdx.x >> 6;
+  const int64_t out_row0 = ((int64_t)rb.layer * a.batch + seq) * a.num_q_heads + rb.head0;
+  // The query rows do not depend on the context length: their loads go out
+  // together with the length's.
+  StageQ<D, QS, NRT, W> sq;
+  static_assert(StageQ<D, QS, NRT, W>::STAGE_BYTES <= lds_slot_bytes<D>(), "q staging");
+  uint8_t* const stage = &ring.ring[wv][0][0];  // free until the first pages are issued
+  sq.issue(stage, static_cast<const uint8_t*>(qp) + out_row0 * D * (QS == 1 ? 2 : 4), rb.nrows, wv,
+           lane);
   const int ctx = clamp_ctx(context_lens[seq], a.max_context, a.max_pages);
   int lo, hi;
   decode_range(ctx, g.window, lo, hi);
-  const int64_t out_row0 = ((int64_t)rb.layer * a.batch + seq) * a.num_q_heads + rb.head0;
 
   if (hi <= lo) {  // empty context: zeros (and no current token to store)
     if (chunk == 0 && wv == 0) {
@@ -696,18 +726,18 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(
     }
     return;
   }
+  // This chunk's pages: the range's np pages split evenly over nch chunks of
+  // at least 16 pages (two per wavefront) where the range allows, then evenly
+  // over the W wavefronts.
   const int p_first = lo >> 4, p_last = (hi - 1) >> 4;
-  const int ppc = g.pages_per_wave * W;
-  const int nch = (p_last - p_first + ppc) / ppc;
+  const int np = p_last - p_first + 1;
+  const int nch = min(g.nchunk, max(1, (np + 2 * W - 1) / (2 * W)));
   if (chunk >= nch) return;
-
-  // Memory traffic in this order: the query rows, this wavefront's page ids
-  // and the current token's rows together, then the first page pair straight
-  // into LDS; q is converted while the pages are in flight.
-  StageQ<D, QS, NRT, W> sq;
-  sq.load(static_cast<const uint8_t*>(qp) + out_row0 * D * (QS == 1 ? 2 : 4), rb.nrows, wv, lane);
-  const int pbeg = p_first + chunk * ppc + wv * g.pages_per_wave;
-  const int pend = min(pbeg + g.pages_per_wave, p_last + 1);
+  // (np <= 2^20 pages and chunk < 2^11 keep the products in 32 bits)
+  const int cbeg = p_first + (int)((uint32_t)(chunk * np) / (uint32_t)nch);
+  const int npc = p_first + (int)((uint32_t)((chunk + 1) * np) / (uint32_t)nch) - cbeg;
+  const int pbeg = cbeg + wv * npc / W;
+  const int pend = cbeg + (wv + 1) * npc / W;
   const int32_t* table_row = block_table + ((int64_t)g.slot * a.batch + seq) * (int64_t)a.max_pages;
   const int ids = pbeg + lane < pend ? table_row[pbeg + lane] : -1;
   auto page_ok = [&](int pi, int& pid) {
@@ -717,6 +747,15 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(
   CurrentToken<D, NK> cur;
   if constexpr (NK != NewKV::kNone)
     cur.load(k_new, v_new, (int64_t)g.slot * a.batch + seq, lane);
+  // q is converted before any page load is issued, so that waiting for it
+  // does not wait for pages (the ids and the current token's rows, issued
+  // after q, are needed right after it anyway).
+  // the staged rows (the oldest loads of this wavefront) have landed
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __builtin_amdgcn_sched_barrier(0);
+  sq.store(sm, stage, rb.nrows, a.scale_log2, wv, lane);
+  __builtin_amdgcn_sched_barrier(0);
   // branch-free: a page that is out of range or has a bad id loads page 0
   // instead (it exists) and is masked later
   auto issue_block = [&](int pa, int slot0) {
@@ -733,10 +772,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(
   // loads, so one constant wait count below finds the oldest block landed.
 #pragma unroll
   for (int i = 0; i < RB - 1; ++i) issue_block(pbeg + 2 * i, 2 * i);
-  __builtin_amdgcn_sched_barrier(0);
-  sq.store(sm, rb.nrows, a.scale_log2, wv, lane);
-  if constexpr (NK != NewKV::kNone) cur.code();
-  __syncthreads();
+  lds_barrier();  // q operands visible to every wavefront; pages stay in flight
   QOps<D, QS, NRT> q;
 #pragma unroll
   for (int n = 0; n < NRT; ++n) {
@@ -759,8 +795,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((RB - 2) * DMA_PER_BLOCK));
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (NK != NewKV::kNone) {
-      if (pa == p_last || pa + 1 == p_last)  // wave-uniform
+      if (pa == p_last || pa + 1 == p_last) {  // wave-uniform: the one wavefront holding it
+        cur.code();
         cur.put(ring.ring[wv][cs + (p_last - pa)], tok, lane);
+      }
     }
     PageRegs<D> c0, c1;
     lds_page<D>(c0, ring.ring[wv][cs], lane, lg);

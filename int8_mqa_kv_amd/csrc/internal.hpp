@@ -28,8 +28,7 @@ struct DecodeGroup {
   int32_t window;
   int32_t first_rb;
   int32_t num_rb;
-  int32_t pages_per_wave;  // even
-  int32_t nchunk;          // chunks per sequence planned for max_context
+  int32_t nchunk;          // chunks (workgroups) per row block and sequence, at most
   int32_t wg_begin;        // first flat workgroup of the group
   int32_t ws_begin;        // first workspace record of the group
   int32_t merge_begin;     // first arrival counter of the group (row blocks x batch before it)
