@@ -196,6 +196,8 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
       }
     G.num_rb = rb - G.first_rb;
     G.nchunk = (int)nchunk[g];
+    G.rb_recip = recip_of((uint32_t)G.num_rb);
+    G.ch_recip = recip_of((uint32_t)G.nchunk);
     G.wg_begin = (int)wg;
     G.ws_begin = (int)ws;
     G.merge_begin = (int)merges;

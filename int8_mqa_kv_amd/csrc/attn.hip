@@ -117,7 +117,7 @@ __device__ __forceinline__ void load_q_raw(QRaw<D, QS, NRT>& r, const void* __re
 
 // Turn the raw rows into int8 matrix-core operands: scale each row by a power
 // of two so that its largest |element| lies in [2^13, 2^14), round to an
-// integer and split it into two int8 halves (split_q15).  Lane (i, g) owns
+// integer and split it into two int8 halves (q15_word, q15_pack4).  Lane (i, g) owns
 // row i's channels g*CH .. g*CH+CH-1, exactly its B-operand bytes.
 template <int D, int QS, int NRT>
 __device__ __forceinline__ void convert_q(QOps<D, QS, NRT>& o, const QRaw<D, QS, NRT>& r,
@@ -154,11 +154,12 @@ __device__ __forceinline__ void convert_q(QOps<D, QS, NRT>& o, const QRaw<D, QS,
     for (int h = 0; h < QOps<D, QS, NRT>::KS8; ++h)
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        int hi[4], lo[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) split_q15(x[16 * h + 4 * d + e] * sc, hi[e], lo[e]);
-        o.q8[n][0][h][d] = pack_i8x4(hi[0], hi[1], hi[2], hi[3]);
-        o.q8[n][1][h][d] = pack_i8x4(lo[0], lo[1], lo[2], lo[3]);
+        const float* xs = x + 16 * h + 4 * d;
+        uint32_t hw, lw;
+        q15_pack4(q15_word(xs[0], sc), q15_word(xs[1], sc), q15_word(xs[2], sc),
+                  q15_word(xs[3], sc), hw, lw);
+        o.q8[n][0][h][d] = hw;
+        o.q8[n][1][h][d] = lw;
       }
   }
 }
@@ -410,16 +411,28 @@ struct DecodeWork {
   int rbl, seq, chunk;
 };
 
+// x / d and x % d (x < 2^31, d >= 1, recip = recip_of(d))
+__device__ __forceinline__ void udiv_recip(uint32_t x, uint32_t d, uint32_t recip, uint32_t& q,
+                                           uint32_t& r) {
+  q = __umulhi(x, recip);
+  r = x - q * d;
+  if (r >= d) {
+    ++q;
+    r -= d;
+  }
+}
+
 __device__ __forceinline__ DecodeWork decode_work(const DecodeArgs& a, int w) {
   int gi = 0;
   while (gi + 1 < a.num_groups && w >= a.groups[gi + 1].wg_begin) ++gi;
   DecodeWork d;
   d.g = a.groups[gi];
-  int local = w - d.g.wg_begin;
-  d.rbl = local % d.g.num_rb;
-  local /= d.g.num_rb;
-  d.chunk = local % d.g.nchunk;
-  d.seq = local / d.g.nchunk;
+  uint32_t q, r;
+  udiv_recip((uint32_t)(w - d.g.wg_begin), (uint32_t)d.g.num_rb, d.g.rb_recip, q, r);
+  d.rbl = (int)r;
+  udiv_recip(q, (uint32_t)d.g.nchunk, d.g.ch_recip, q, r);
+  d.chunk = (int)r;
+  d.seq = (int)q;
   d.rb = a.rbs[d.g.first_rb + d.rbl];
   return d;
 }
@@ -434,12 +447,24 @@ __device__ __forceinline__ DecodeWork decode_work(const DecodeArgs& a, int w) {
 template <int D>
 constexpr int lds_slot_bytes() { return page_bytes(D) + 128; }
 
+// One 1 KiB piece of a record at byte OFF: the instruction offset applies to
+// both the global and the LDS address, so every piece of a page shares one
+// address computation and one LDS base.
+template <int OFF>
+__device__ __forceinline__ void dma_kib(const uint8_t* lane_src, uint8_t* lds_slot) {
+  __builtin_amdgcn_global_load_lds(lane_src, lds_slot, 16, OFF, 0);
+}
+
 template <int D>
 __device__ __forceinline__ void dma_page(uint8_t* lds_slot, const uint8_t* __restrict__ rec,
                                          int lane) {
-#pragma unroll
-  for (int h = 0; h < 32 * D / 1024; ++h)
-    __builtin_amdgcn_global_load_lds(rec + h * 1024 + lane * 16, lds_slot + h * 1024, 16, 0, 0);
+  const uint8_t* src = rec + lane * 16;
+  dma_kib<0>(src, lds_slot);
+  dma_kib<1024>(src, lds_slot);
+  if constexpr (D == 128) {
+    dma_kib<2048>(src, lds_slot);
+    dma_kib<3072>(src, lds_slot);
+  }
   // the 128 bytes of fp32 scales: 4 bytes per lane; lanes 32..63 re-read the
   // last scale and land in the slot's padding (no branch, no exec change)
   __builtin_amdgcn_global_load_lds(rec + 32 * D + 4 * min(lane, 31), lds_slot + 32 * D, 4, 0, 0);
@@ -585,13 +610,9 @@ struct StageQ {
       const int lg = c0 / CH, h = (c0 % CH) >> 4, e0 = c0 & 15;
       uint32_t hw[PER / 4], lw[PER / 4];
 #pragma unroll
-      for (int d = 0; d < PER / 4; ++d) {
-        int hi[4], lo[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) split_q15(x[4 * d + e] * sc, hi[e], lo[e]);
-        hw[d] = pack_i8x4(hi[0], hi[1], hi[2], hi[3]);
-        lw[d] = pack_i8x4(lo[0], lo[1], lo[2], lo[3]);
-      }
+      for (int d = 0; d < PER / 4; ++d)
+        q15_pack4(q15_word(x[4 * d], sc), q15_word(x[4 * d + 1], sc), q15_word(x[4 * d + 2], sc),
+                  q15_word(x[4 * d + 3], sc), hw[d], lw[d]);
       uint32_t* dh = reinterpret_cast<uint32_t*>(&sm.q8[n][0][h][16 * lg + li]) + e0 / 4;
       uint32_t* dl = reinterpret_cast<uint32_t*>(&sm.q8[n][1][h][16 * lg + li]) + e0 / 4;
       if constexpr (PER == 8) {

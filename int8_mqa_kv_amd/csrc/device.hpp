@@ -64,18 +64,23 @@ __device__ __forceinline__ i32x4 mma_i8(const u32x4& a, const u32x4& b, const i3
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(bitcast<i32x4>(a), bitcast<i32x4>(b), c, 0, 0, 0);
 }
 
-// A query element as a 15-bit fixed-point integer split into two int8 halves:
-// v = rint(y) with |y| < 2^14, hi = (v + 128) >> 8 in [-64, 64],
-// lo = v - 256*hi in [-128, 127]; v = 256*hi + lo exactly.
-__device__ __forceinline__ void split_q15(float y, int& hi, int& lo) {
-  const int v = (int)__builtin_rintf(y);
-  hi = (v + 128) >> 8;
-  lo = v - (hi << 8);
+// A query element as a 15-bit fixed-point integer v = rint(x * sc)
+// (|x * sc| < 2^14) split into two int8 halves v = 256*hi + lo with
+// hi = floor((v + 128) / 256) in [-64, 64] and lo = v - 256*hi in [-128, 127].
+// fma(x, sc, 1.5*2^23 + 128) lands on the fp32 grid of spacing 1 (the FMA
+// rounds half to even, as rint does), so the low 16 bits of its bits hold
+// t = v + 128 in two's complement: byte 1 of t is hi, byte 0 xor 0x80 is lo.
+__device__ __forceinline__ uint32_t q15_word(float x, float sc) {
+  return bitcast<uint32_t>(__builtin_fmaf(x, sc, 12583040.0f));  // 1.5*2^23 + 128
 }
-
-__device__ __forceinline__ uint32_t pack_i8x4(int a, int b, int c, int d) {
-  return (uint32_t)(a & 255) | ((uint32_t)(b & 255) << 8) | ((uint32_t)(c & 255) << 16) |
-         ((uint32_t)d << 24);
+// hi and lo int8 halves of four q15_words, packed (element k = byte k)
+__device__ __forceinline__ void q15_pack4(uint32_t t0, uint32_t t1, uint32_t t2, uint32_t t3,
+                                          uint32_t& hi, uint32_t& lo) {
+  // v_perm_b32 selector bytes 0-3 pick the second operand's bytes, 4-7 the first's
+  const uint32_t a = __builtin_amdgcn_perm(t1, t0, 0x05010400u);  // t0.b0 t1.b0 t0.b1 t1.b1
+  const uint32_t b = __builtin_amdgcn_perm(t3, t2, 0x05010400u);  // t2.b0 t3.b0 t2.b1 t3.b1
+  lo = __builtin_amdgcn_perm(b, a, 0x05040100u) ^ 0x80808080u;
+  hi = __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
 // Reductions across the four lanes i, i+16, i+32, i+48 (one matrix row) with

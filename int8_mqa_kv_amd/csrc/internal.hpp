@@ -33,7 +33,14 @@ struct DecodeGroup {
   int32_t ws_begin;        // first workspace record of the group
   int32_t merge_begin;     // first arrival counter of the group (row blocks x batch before it)
   int32_t writes_new_kv;   // this group stores the slot's current token (first group of a slot)
+  uint32_t rb_recip;       // floor((2^32 - 1) / num_rb): division by num_rb (udiv_recip)
+  uint32_t ch_recip;       // floor((2^32 - 1) / nchunk)
 };
+
+// x / d for x < 2^31 and d >= 1 given recip = floor((2^32 - 1) / d): the
+// high half of x * recip undershoots x / d by at most one, which one
+// correction step repairs.
+MQA_HD inline uint32_t recip_of(uint32_t d) { return 0xFFFFFFFFu / d; }
 
 struct DecodeArgs {
   int64_t num_pages;
