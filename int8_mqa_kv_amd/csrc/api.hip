@@ -402,7 +402,7 @@ int mqa_append_attn(const void* q, mqa_dtype q_dtype, float* out, const mqa_kv_p
   AppendArgs a;
   memset(&a, 0, sizeof a);
   const int head_blocks = (num_q_heads + kRowsPerBlock - 1) / kRowsPerBlock;
-  const int token_blocks = (max_q_len + kAttnWaves - 1) / kAttnWaves;
+  const int token_blocks = (max_q_len + kAppendWaves - 1) / kAppendWaves;
   const int64_t total = (int64_t)num_layers * batch * head_blocks * token_blocks;
   if (total > (INT64_C(1) << 31) - 8) return fail(MQA_ERR_UNSUPPORTED, "launch too large");
   // layers ordered by slot, so layers sharing a slot run back to back
@@ -425,6 +425,9 @@ int mqa_append_attn(const void* q, mqa_dtype q_dtype, float* out, const mqa_kv_p
   a.head_blocks = head_blocks;
   a.token_blocks = token_blocks;
   a.total_wgs = (int)total;
+  a.tb_recip = recip_of((uint32_t)token_blocks);
+  a.hb_recip = recip_of((uint32_t)head_blocks);
+  a.layer_recip = recip_of((uint32_t)num_layers);
   a.scale_log2 = scale_log2_of(softmax_scale, pool->head_dim);
   const int nrt = num_q_heads <= 16 ? 1 : 2;
   AppendPtrs ptrs;

@@ -322,68 +322,6 @@ __device__ __forceinline__ void attend_block_any(WaveState<D, NRT>& st, const QO
     attend_block<D, QS, NRT, false>(st, q, p0, p1, ok0, ok1, pos0, lo, hi, lg);
 }
 
-// Logical pages [pbeg, pend) of one (slot, sequence), read two at a time.
-// The wavefront keeps a window of 64 page ids in a register (lane i holds the
-// id of page wbase + i), filled by one coalesced load and handed out with
-// readlane, so the page loads never wait on a table read of their own.
-template <int D>
-struct PageStream {
-  const uint8_t* __restrict__ pool;
-  const int32_t* __restrict__ table_row;
-  int64_t num_pages;
-  int pend;
-  int lane, lg;
-  int ids, wbase;
-  PageRegs<D> c0, c1;
-  bool ok0, ok1;
-
-  __device__ __forceinline__ void load_ids(int from) {
-    wbase = from;
-    ids = from + lane < pend ? table_row[from + lane] : -1;
-  }
-  // Branch-free: a page outside [.., pend) or with an id outside the pool
-  // loads page 0 instead (it exists: num_pages >= 1) and is masked by ok.
-  template <bool RELOAD>
-  __device__ __forceinline__ void fetch(PageRegs<D>& r, int pi, bool& ok) {
-    if constexpr (RELOAD) {
-      if (pi - wbase >= 64) load_ids(pi);
-    }
-    const int pid = __builtin_amdgcn_readlane(ids, min(pi - wbase, 63));
-    ok = pi < pend && (uint32_t)pid < (uint64_t)num_pages;
-    load_page<D>(r, pool + (int64_t)(ok ? pid : 0) * page_bytes(D), lane, lg);
-  }
-  // issue the first pair's loads
-  template <bool RELOAD>
-  __device__ __forceinline__ void start(int pbeg) {
-    fetch<RELOAD>(c0, pbeg, ok0);
-    fetch<RELOAD>(c1, pbeg + 1, ok1);
-  }
-};
-
-// Attend pages [pbeg, ps.pend) whose first pair ps.start(pbeg) already issued;
-// the next pair's loads are issued before the current pair is computed.
-template <int D, int QS, int NRT, bool RELOAD>
-__device__ __forceinline__ void attend_pages(WaveState<D, NRT>& st, const QOps<D, QS, NRT>& q,
-                                             PageStream<D>& ps, int pbeg, int lo, int hi) {
-  for (int pa = pbeg; pa < ps.pend; pa += 2) {
-    PageRegs<D> n0, n1;
-    bool nok0 = false, nok1 = false;
-    const bool more = pa + 2 < ps.pend;
-    if (more) {
-      ps.template fetch<RELOAD>(n0, pa + 2, nok0);
-      ps.template fetch<RELOAD>(n1, pa + 3, nok1);
-    }
-    attend_block_any<D, QS, NRT>(st, q, ps.c0, ps.c1, ps.ok0, ps.ok1, pa * kPageTokens, lo, hi,
-                                 ps.lg);
-    if (more) {
-      ps.c0 = n0;
-      ps.c1 = n1;
-      ps.ok0 = nok0;
-      ps.ok1 = nok1;
-    }
-  }
-}
-
 __device__ __forceinline__ int clamp_ctx(int ctx, int max_context, int max_pages) {
   const int cap = min(max_context, max_pages * kPageTokens);
   return min(max(ctx, 0), cap);
@@ -988,27 +926,49 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Append: one wavefront = all heads of a row block for one chunk token; the
-// workgroup's four wavefronts take four consecutive tokens (their key ranges
-// nearly coincide, so their page reads hit the same cache lines).
+// Append: one workgroup = W consecutive tokens of one (layer, sequence, row
+// block), one wavefront per token carrying that token's heads.  The tokens'
+// key ranges nearly coincide, so the workgroup streams the union of their
+// pages HBM -> LDS once, through a ring of RB two-page blocks shared by all
+// wavefronts: each block's 1 KiB pieces and scale blocks are spread over the
+// wavefronts, and one barrier per block both publishes a landed block and
+// frees the slot the next load reuses.  Each wavefront masks the keys to its
+// own token's causal (and window) range.
 // ---------------------------------------------------------------------------
+template <int D>
+struct AppendGeo {
+  static constexpr int KIB = 32 * D / 1024;        // 1 KiB code pieces per page
+  static constexpr int PIECES = 2 * KIB + 2;       // per block: code pieces + two scale blocks
+};
+
+template <int D, int W, int RB>
+struct alignas(16) AppendLds {
+  uint8_t ring[RB][2][lds_slot_bytes<D>()];
+  int ok[RB][2];  // page of the slot exists (in range, id inside the pool)
+};
+
 template <int D, int QS, int NRT>
-__global__ __launch_bounds__(kAttnWaves * 64) void append_kernel(
+__global__ __launch_bounds__(kAppendWaves * 64) void append_kernel(
     const AppendArgs a, const void* __restrict__ qp, float* __restrict__ out,
     const uint8_t* __restrict__ pool, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ cu_q_lens) {
+  constexpr int W = kAppendWaves, RB = kAppendRing;
   constexpr int VT = Geo<D>::VT;
+  constexpr int KIB = AppendGeo<D>::KIB, PIECES = AppendGeo<D>::PIECES;
+  constexpr int MY_PIECES_MAX = (PIECES + W - 1) / W;
+  __shared__ AppendLds<D, W, RB> sm;
   const int w = swizzled_block();
   if (w >= a.total_wgs) return;
-  int local = w;
-  const int tb = local % a.token_blocks;
-  local /= a.token_blocks;
-  const int hb = local % a.head_blocks;
-  local /= a.head_blocks;
+  uint32_t q_, r_;
+  udiv_recip((uint32_t)w, (uint32_t)a.token_blocks, a.tb_recip, q_, r_);
+  const int tb = (int)r_;
+  udiv_recip(q_, (uint32_t)a.head_blocks, a.hb_recip, q_, r_);
+  const int hb = (int)r_;
   // layers are enumerated innermost after the sequence so that the layers
   // sharing a slot (adjacent in a.order) read the same pages back to back
-  const int oi = local % a.num_layers;
-  const int seq = local / a.num_layers;
+  udiv_recip(q_, (uint32_t)a.num_layers, a.layer_recip, q_, r_);
+  const int oi = (int)r_;
+  const int seq = (int)q_;
   const int layer = a.order[oi];
   const int slot = a.layer_slot[layer];
   const int window = a.layer_window[layer];
@@ -1017,46 +977,111 @@ __global__ __launch_bounds__(kAttnWaves * 64) void append_kernel(
   const int wv = threadIdx.x >> 6;
   const int q0 = cu_q_lens[seq];
   const int qlen = cu_q_lens[seq + 1] - q0;
-  const int t = tb * kAttnWaves + wv;
-  if (t >= qlen || q0 < 0 || q0 + t >= a.total_q) return;
+  const int t0 = tb * W;
+  if (t0 >= qlen || q0 < 0 || q0 + qlen > a.total_q) return;  // workgroup-uniform
+  const int nt = min(W, qlen - t0);                            // tokens of this workgroup
   const int ctx = clamp_ctx(context_lens[seq], a.max_context, a.max_pages);
-  const int p = ctx - qlen + t;
+  const int t = t0 + wv;
+  const bool live = wv < nt;
+  const int p = ctx - qlen + t;  // this wavefront's position
   const int head0 = hb * kRowsPerBlock;
   const int nrows = min(kRowsPerBlock, a.num_q_heads - head0);
-  const int64_t row0 = ((int64_t)layer * a.total_q + q0 + t) * a.num_q_heads + head0;
-  if (p < 0) {
-    for (int n = 0; n < NRT; ++n) {
-      const int row = 16 * n + li;
-      if (row < nrows)
-        for (int tt = 0; tt < VT; ++tt)
-          *reinterpret_cast<f32x4*>(out + (row0 + row) * D + 16 * tt + 4 * lg) =
-              f32x4{0, 0, 0, 0};
-    }
+  const int64_t row0 = ((int64_t)layer * a.total_q + q0 + min(t, qlen - 1)) * a.num_q_heads + head0;
+
+  // the union of the tokens' key ranges
+  const int p_lo = ctx - qlen + t0, p_hi = ctx - qlen + t0 + nt - 1;
+  const int lo_u = window > 0 ? max(0, p_lo - window + 1) : 0;
+  const int hi_u = p_hi + 1;
+  if (hi_u <= 0 || lo_u >= hi_u) {  // no key at all (context shorter than the chunk)
+    if (live)
+      for (int n = 0; n < NRT; ++n) {
+        const int row = 16 * n + li;
+        if (row < nrows)
+          for (int tt = 0; tt < VT; ++tt)
+            *reinterpret_cast<f32x4*>(out + (row0 + row) * D + 16 * tt + 4 * lg) =
+                f32x4{0, 0, 0, 0};
+      }
     return;
   }
+  const int pbeg = lo_u >> 4, pend = ((hi_u - 1) >> 4) + 1;
+  const int nblk = (pend - pbeg + 1) >> 1;
+  // this wavefront's own key range (positions below 0 have no keys)
   const int hi = p + 1;
   const int lo = window > 0 ? max(0, p - window + 1) : 0;
 
+  // q first (converted before any page load is issued, so that its wait does
+  // not also wait for pages)
   constexpr int esz = QS == 1 ? 2 : 4;
   QRaw<D, QS, NRT> qr;
   load_q_raw<D, QS, NRT>(qr, static_cast<const uint8_t*>(qp) + row0 * D * esz, nrows, li, lg);
-  const int pbeg = lo >> 4;
-  PageStream<D> ps;
-  ps.pool = pool;
-  ps.table_row = block_table + ((int64_t)slot * a.batch + seq) * (int64_t)a.max_pages;
-  ps.num_pages = a.num_pages;
-  ps.pend = ((hi - 1) >> 4) + 1;
-  ps.lane = lane;
-  ps.lg = lg;
-  ps.load_ids(pbeg);
-  ps.template start<true>(pbeg);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
   QOps<D, QS, NRT> q;
   convert_q<D, QS, NRT>(q, qr, a.scale_log2, nrows, li);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // page ids, a window of 64 per register, reloaded when the loads pass it
+  const int32_t* table_row = block_table + ((int64_t)slot * a.batch + seq) * (int64_t)a.max_pages;
+  int wbase = pbeg;
+  int ids = pbeg + lane < pend ? table_row[pbeg + lane] : -1;
+  // this wavefront's share of block `blk`'s loads into ring slot `rs`
+  auto issue_block = [&](int blk, int rs) {
+#pragma unroll
+    for (int i = 0; i < MY_PIECES_MAX; ++i) {
+      const int k = wv + i * W;
+      if (k >= PIECES) break;  // wave-uniform
+      const int u = k < 2 * KIB ? k / KIB : k - 2 * KIB;
+      const int pg = pbeg + 2 * blk + u;
+      if (pg - wbase >= 64) {  // wave-uniform
+        wbase = pg;
+        ids = pg + lane < pend ? table_row[pg + lane] : -1;
+      }
+      const int pid = __builtin_amdgcn_readlane(ids, min(max(pg - wbase, 0), 63));
+      const bool ok = pg < pend && (uint32_t)pid < (uint64_t)a.num_pages;
+      const uint8_t* rec = pool + (int64_t)(ok ? pid : 0) * page_bytes(D);
+      uint8_t* dst = sm.ring[rs][u];
+      if (k < 2 * KIB) {
+        const int h = k % KIB;
+        __builtin_amdgcn_global_load_lds(rec + h * 1024 + lane * 16, dst + h * 1024, 16, 0, 0);
+        if (h == 0 && lane == 0) sm.ok[rs][u] = ok;
+      } else {
+        __builtin_amdgcn_global_load_lds(rec + 32 * D + 4 * min(lane, 31), dst + 32 * D, 4, 0, 0);
+      }
+    }
+  };
+  // loads per block issued by this wavefront (constant: every block issues
+  // all its pieces; blocks past the range load page 0, unused)
+  const int mine = (PIECES - wv + W - 1) / W;
+#pragma unroll
+  for (int i = 0; i < RB - 1; ++i) issue_block(i, i);
+
   WaveState<D, NRT> st;
   st.init();
-  attend_pages<D, QS, NRT, true>(st, q, ps, pbeg, lo, hi);
+  for (int b = 0; b < nblk; ++b) {
+    const int rs = b % RB;
+    // this wavefront's pieces of block b have landed (blocks b+1 .. b+RB-2
+    // may still be in flight) ...
+    // (a page-id reload among the younger loads only makes this wait longer)
+    static_assert(MY_PIECES_MAX <= 2, "wait counts below");
+    if (mine == 2) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((RB - 2) * 2));
+    } else if (mine == 1) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((RB - 2) * 1));
+    }
+    // ... and, past the barrier, every wavefront's; every wavefront is also
+    // done with the slot that block b+RB-1 now reuses
+    lds_barrier();
+    issue_block(b + RB - 1, (b + RB - 1) % RB);
+    if (live) {
+      PageRegs<D> c0, c1;
+      lds_page<D>(c0, sm.ring[rs][0], lane, lg);
+      lds_page<D>(c1, sm.ring[rs][1], lane, lg);
+      const int pos0 = (pbeg + 2 * b) * kPageTokens;
+      attend_block_any<D, QS, NRT>(st, q, c0, c1, sm.ok[rs][0] != 0, sm.ok[rs][1] != 0, pos0, lo,
+                                   hi, lg);
+    }
+  }
+  // every load of this wavefront has landed before the workgroup exits
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  if (!live) return;
 #pragma unroll
   for (int n = 0; n < NRT; ++n) {
     const int row = 16 * n + li;
@@ -1106,7 +1131,7 @@ hipError_t launch_decode(int D, bool q_f32, int nrt, NewKV nk, const DecodeArgs&
 
 template <int D, int QS, int NRT>
 static hipError_t launch_append_t(const AppendArgs& a, const AppendPtrs& p, hipStream_t stream) {
-  hipLaunchKernelGGL((append_kernel<D, QS, NRT>), padded_grid(a.total_wgs), dim3(kAttnWaves * 64),
+  hipLaunchKernelGGL((append_kernel<D, QS, NRT>), padded_grid(a.total_wgs), dim3(kAppendWaves * 64),
                      0, stream, a, p.q, p.out, p.pool, p.block_table, p.context_lens, p.cu_q_lens);
   return hipGetLastError();
 }

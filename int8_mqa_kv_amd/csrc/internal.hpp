@@ -7,7 +7,8 @@
 
 namespace mqa {
 
-constexpr int kAttnWaves = 4;       // wavefronts per attention workgroup
+constexpr int kAppendWaves = 8;     // wavefronts (tokens) per append workgroup
+constexpr int kAppendRing = 4;      // two-page blocks in an append workgroup's ring
 constexpr int kRowsPerBlock = 32;   // query rows (heads) one wavefront carries
 constexpr int kMaxGroups = 24;      // (slot, window) groups per decode launch
 constexpr int kMaxRowBlocks = 64;   // row blocks per decode launch
@@ -81,8 +82,9 @@ struct AppendArgs {
   int32_t total_q;
   int32_t num_layers;
   int32_t head_blocks;     // ceil(num_q_heads / 32)
-  int32_t token_blocks;    // ceil(max_q_len / kAttnWaves)
+  int32_t token_blocks;    // ceil(max_q_len / kAppendWaves)
   int32_t total_wgs;
+  uint32_t tb_recip, hb_recip, layer_recip;  // recip_of(token_blocks / head_blocks / num_layers)
   float scale_log2;
   // layers in launch order (grouped by slot); order[i] is a layer index
   int32_t order[kMaxLayers];
