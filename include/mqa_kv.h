@@ -145,9 +145,10 @@ int kv_pack_int8(const void* k, const void* v, mqa_dtype src_dtype,
  * Workspace for mqa_decode_attn / mqa_decode_step with the same shape
  * arguments (the host arrays are read).  Contexts long enough to be split
  * across workgroups leave softmax partials (max, sum, weighted values) there;
- * the workgroup that arrives last merges them inside the same kernel.  The
- * first 256 KiB of a workspace hold the arrival counters (one per 32-head row
- * block of a layer and sequence, at most 65536 per call), the partials follow.
+ * the last of them to arrive merges them inside the same kernel.  The first
+ * 8 MiB of a workspace hold the arrival counters (8 per 32-head row block of
+ * a layer and sequence, each on its own 128-byte line; at most 8192 such
+ * pairs per call), the partials follow.
  * Returns 0 when none is needed or the arguments are invalid (a following
  * call reports why).  The workspace must be zero-filled ONCE before its first
  * use (e.g. hipMemset after allocation); every call leaves the counters at

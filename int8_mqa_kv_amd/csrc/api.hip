@@ -215,13 +215,13 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
   a.total_merge = (int)merges;
   if (split) {
     // the fixed counter prefix, then the partial records
-    if (merges > kDecodeCounters) {
+    if (merges * kDecodeWaves > kDecodeCounters) {
       p.rc = fail(MQA_ERR_UNSUPPORTED,
                   "%lld (row block, sequence) pairs with split contexts in one call; at most %lld",
-                  (long long)merges, (long long)kDecodeCounters);
+                  (long long)merges, (long long)(kDecodeCounters / kDecodeWaves));
       return p;
     }
-    p.ws_bytes = (size_t)(kDecodeCounters + ws * ws_record_floats(head_dim)) * sizeof(float);
+    p.ws_bytes = (size_t)(kCounterWords + ws * ws_record_floats(head_dim)) * sizeof(float);
   }
   return p;
 }

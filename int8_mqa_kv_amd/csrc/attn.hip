@@ -433,7 +433,6 @@ struct DecodeQLds {
   float m[W][32];
   float l[W][32];
   int ev[W];
-  int last;
 };
 // Each wavefront's ring of RB blocks of two pages.  Once its pages are
 // consumed, a wavefront dumps its accumulators into its own ring for the
@@ -840,40 +839,43 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(
     return;
   }
 
-  // ---- several chunks: publish this chunk's partial record ----
+  // ---- several chunks: each wavefront publishes its pairs of the chunk's
+  // record and counts its own arrival; for each wavefront index the last of
+  // the chunks to arrive merges those pairs over all chunks.  No workgroup
+  // barrier lies on this path. ----
   constexpr int64_t RS = ws_record_floats(D);
+  constexpr int PF = kPairFloats;  // per pair: m[16], l[16], acc[4][64]
+  const int64_t item = (int64_t)g.merge_begin + (int64_t)dw.rbl * a.batch + seq;
   const int64_t rec0 = (int64_t)g.ws_begin + ((int64_t)dw.rbl * a.batch + seq) * g.nchunk;
-  float* const recs = ws + kDecodeCounters;
+  if (wv >= PAIRS) return;  // (head_dim 64 with 16 rows: no pair for this wavefront)
+  float* const recs = ws + kCounterWords;
   float* mine = recs + (rec0 + chunk) * RS;
 #pragma unroll
   for (int k = 0; k < PPW; ++k) {
     const int pi = wv + k * W;
     if (pi >= PAIRS) continue;
-    const int row = 16 * (pi / VT) + li;
-    if (pi % VT == 0 && lg == 0) {
-      st_dev(mine + row, Mr[k]);
-      st_dev(mine + 32 + row, Lr[k]);
+    float* pr = mine + pi * PF;
+    if (lg == 0) {
+      st_dev(pr + li, Mr[k]);
+      st_dev(pr + 16 + li, Lr[k]);
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) st_dev(mine + 64 + (pi * 4 + e) * 64 + lane, Ar[k][e]);
+    for (int e = 0; e < 4; ++e) st_dev(pr + 32 + e * 64 + lane, Ar[k][e]);
   }
-  // every wavefront's stores have completed before the arrival is counted
+  // the stores have completed before the arrival is counted
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t* cnt = reinterpret_cast<uint32_t*>(ws) + g.merge_begin + (int64_t)dw.rbl * a.batch +
-                    seq;
-    const uint32_t before = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-    const int last = before == (uint32_t)(nch - 1);
-    // the last arrival leaves the counter at zero for the next call
-    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sm.last = last;
-  }
-  __syncthreads();
-  if (!sm.last) return;
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(ws) + (item * W + wv) * kCounterStride;
+  uint32_t before = 0;
+  if (lane == 0)
+    before = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  before = __builtin_amdgcn_readfirstlane(before);
+  if (before != (uint32_t)(nch - 1)) return;
+  // the last arrival leaves the counter at zero for the next call
+  if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // ---- the last chunk to arrive: fold all records in chunk order ----
+  // ---- this wavefront's pairs over all chunks, folded in chunk order ----
   // (the order, not the arrival, fixes the rounding: results are deterministic)
   constexpr int CB = 8;  // records loaded per round trip
   float M[PPW], L[PPW];
@@ -890,14 +892,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(
 #pragma unroll
     for (int k = 0; k < PPW; ++k) {
       const int pi = min(wv + k * W, PAIRS - 1);
-      const int row = 16 * (pi / VT) + li;
 #pragma unroll
       for (int u = 0; u < CB; ++u) {
-        const float* r = recs + (rec0 + min(c0 + u, nch - 1)) * RS;
-        mc[k][u] = ld_dev(r + row);
-        lc[k][u] = ld_dev(r + 32 + row);
+        const float* r = recs + (rec0 + min(c0 + u, nch - 1)) * RS + pi * PF;
+        mc[k][u] = ld_dev(r + li);
+        lc[k][u] = ld_dev(r + 16 + li);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ac[k][u][e] = ld_dev(r + 64 + (pi * 4 + e) * 64 + lane);
+        for (int e = 0; e < 4; ++e) ac[k][u][e] = ld_dev(r + 32 + e * 64 + lane);
       }
     }
 #pragma unroll

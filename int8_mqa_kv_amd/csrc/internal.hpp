@@ -112,14 +112,20 @@ hipError_t launch_append(int D, bool q_f32, int nrt, const AppendArgs& a, const 
                          hipStream_t stream);
 
 // Decode workspace: a fixed prefix of 32-bit arrival counters, one per
-// (row block, sequence) of a call, then one partial record per (row block,
-// sequence, chunk) of a split sequence -- m[32], l[32] and acc[32 * D] fp32,
-// acc in matrix-core operand order ((16-row tile, 16-channel tile, element) x
-// 64 lanes).  The counter prefix has the same size and place for every call
-// shape, so calls of different shapes can share one workspace: each leaves
-// its counters at zero and records never overwrite a counter.
-constexpr int64_t ws_record_floats(int D) { return kRowsPerBlock * (D + 2); }
-constexpr int64_t kDecodeCounters = 65536;  // 256 KiB
+// (row block, sequence, wavefront) of a call and each on a 128-byte line of
+// its own (atomics to one line serialise), then one partial record per
+// (row block, sequence, chunk) of a split sequence.  A record holds, for each
+// (16-row tile, 16-channel tile) pair of the output, m[16], l[16] and
+// acc[4][64] fp32 (acc in matrix-core operand order), so that one wavefront
+// writes and reads its pairs with whole 256-byte accesses.  The counter
+// prefix has the same size and place for every call shape, so calls of
+// different shapes can share one workspace: each leaves its counters at zero
+// and records never overwrite a counter.
+constexpr int kPairFloats = 16 + 16 + 4 * 64;
+constexpr int64_t ws_record_floats(int D) { return (int64_t)2 * (D / 16) * kPairFloats; }
+constexpr int64_t kDecodeCounters = 65536;        // arrival counters per call, at most
+constexpr int64_t kCounterStride = 32;            // 32-bit words per counter (128 bytes)
+constexpr int64_t kCounterWords = kDecodeCounters * kCounterStride;  // 8 MiB prefix
 constexpr int kDecodeWaves = 8;     // wavefronts per decode workgroup
 constexpr int kDecodeRing = 2;      // blocks of two pages in flight per wavefront
 

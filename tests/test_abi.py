@@ -105,11 +105,11 @@ def test_decode_workspace_sizes():
     # short local window: one chunk per sequence, no workspace
     ws1 = mk.decode_workspace_bytes(64, 32, [0], [1024], 4096, 128)
     ws2 = mk.decode_workspace_bytes(16, 32, [0], [0], 32768, 128)
-    # several chunks per sequence: partial records (32 rows x (d + 2) fp32
-    # each, at least two per sequence) plus one 4-byte arrival counter per
-    # sequence, rounded up to 256 bytes
+    # several chunks per sequence: an 8 MiB prefix of arrival counters, then
+    # partial records (16 (row tile, channel tile) pairs x 288 fp32 each at
+    # d = 128, at least two records per sequence)
     assert ws2 % 256 == 0
-    assert ws2 >= 16 * (2 * 32 * 130 * 4 + 4)
+    assert ws2 >= (8 << 20) + 16 * 2 * 16 * 288 * 4
     assert mk.lib.mqa_decode_workspace_bytes(0, 32, 1, None, None, 4096, 128) == 0
     assert ws1 >= 0
 
