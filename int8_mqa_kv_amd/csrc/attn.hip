@@ -984,7 +984,10 @@ __global__ __launch_bounds__(kAppendWaves * 64) void append_kernel(
   const int ctx = clamp_ctx(context_lens[seq], a.max_context, a.max_pages);
   const int t = t0 + wv;
   const bool live = wv < nt;
-  const int p = ctx - qlen + t;  // this wavefront's position
+  // this wavefront's position; a wavefront past the chunk's last token runs
+  // that token's key range (valid data, no branch around the attention) and
+  // writes nothing
+  const int p = ctx - qlen + min(t, t0 + nt - 1);
   const int head0 = hb * kRowsPerBlock;
   const int nrows = min(kRowsPerBlock, a.num_q_heads - head0);
   const int64_t row0 = ((int64_t)layer * a.total_q + q0 + min(t, qlen - 1)) * a.num_q_heads + head0;
@@ -1071,14 +1074,12 @@ __global__ __launch_bounds__(kAppendWaves * 64) void append_kernel(
     // done with the slot that block b+RB-1 now reuses
     lds_barrier();
     issue_block(b + RB - 1, (b + RB - 1) % RB);
-    if (live) {
-      PageRegs<D> c0, c1;
-      lds_page<D>(c0, sm.ring[rs][0], lane, lg);
-      lds_page<D>(c1, sm.ring[rs][1], lane, lg);
-      const int pos0 = (pbeg + 2 * b) * kPageTokens;
-      attend_block_any<D, QS, NRT>(st, q, c0, c1, sm.ok[rs][0] != 0, sm.ok[rs][1] != 0, pos0, lo,
-                                   hi, lg);
-    }
+    PageRegs<D> c0, c1;
+    lds_page<D>(c0, sm.ring[rs][0], lane, lg);
+    lds_page<D>(c1, sm.ring[rs][1], lane, lg);
+    const int pos0 = (pbeg + 2 * b) * kPageTokens;
+    attend_block_any<D, QS, NRT>(st, q, c0, c1, sm.ok[rs][0] != 0, sm.ok[rs][1] != 0, pos0, lo, hi,
+                                 lg);
   }
   // every load of this wavefront has landed before the workgroup exits
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
