@@ -335,8 +335,11 @@ __device__ __forceinline__ void decode_range(int ctx, int window, int& lo, int& 
 
 // XCD-aware flat index: hardware workgroup x runs on XCD x % 8, so give each
 // XCD a contiguous range of logical work (gridDim.x is a multiple of 8).
-__device__ __forceinline__ int swizzled_block() {
-  const int nx = gridDim.x, x = blockIdx.x;
+// The grid is total rounded up to a multiple of 8 (padded_grid); taking its
+// size from the launch's own total keeps the read in the same batch as the
+// other kernel arguments.
+__device__ __forceinline__ int swizzled_block(int total) {
+  const int nx = (total + 7) & ~7, x = blockIdx.x;
   return (x & 7) * (nx >> 3) + (x >> 3);
 }
 
@@ -360,18 +363,48 @@ __device__ __forceinline__ void udiv_recip(uint32_t x, uint32_t d, uint32_t reci
   }
 }
 
+// The workgroup's (group, row block, chunk, sequence).  Kernel arguments are
+// read with scalar loads whose round trips add up when one address depends on
+// another, so every field the usual launches need sits at a fixed offset and
+// is read in one batch: the first four groups' first workgroups, group 0 and
+// its first row block.  Other workgroups read their group or row block at a
+// computed offset, one round trip later.
+// A kernel's first argument, read in place in the kernel-argument segment
+// (the first argument sits at offset 0).  Indexing a by-value argument with a
+// computed index makes the compiler copy the whole struct out of that segment
+// first; reading through this pointer does not.
+template <typename T>
+__device__ __forceinline__ const T* first_kernel_arg() {
+  // (a C-style cast: from the constant address space to a generic pointer)
+  return (const T*)__builtin_amdgcn_kernarg_segment_ptr();
+}
+
 __device__ __forceinline__ DecodeWork decode_work(const DecodeArgs& a, int w) {
-  int gi = 0;
-  while (gi + 1 < a.num_groups && w >= a.groups[gi + 1].wg_begin) ++gi;
+  const DecodeArgs* ka = first_kernel_arg<DecodeArgs>();
+  const int ng = a.num_groups;
+  const int wb1 = a.wg_begin4[1], wb2 = a.wg_begin4[2], wb3 = a.wg_begin4[3];
+  const DecodeGroup g0 = a.groups[0];
+  const RowBlock r0 = a.rbs[0];
+  int gi = (ng > 1 && w >= wb1) + (ng > 2 && w >= wb2) + (ng > 3 && w >= wb3);
   DecodeWork d;
-  d.g = a.groups[gi];
+  if (gi == 0) {
+    d.g = g0;
+  } else {
+    if (gi == 3)
+      while (gi + 1 < ng && w >= ka->groups[gi + 1].wg_begin) ++gi;
+    d.g = ka->groups[gi];
+  }
   uint32_t q, r;
   udiv_recip((uint32_t)(w - d.g.wg_begin), (uint32_t)d.g.num_rb, d.g.rb_recip, q, r);
   d.rbl = (int)r;
   udiv_recip(q, (uint32_t)d.g.nchunk, d.g.ch_recip, q, r);
   d.chunk = (int)r;
   d.seq = (int)q;
-  d.rb = a.rbs[d.g.first_rb + d.rbl];
+  const int rbi = d.g.first_rb + d.rbl;
+  if (rbi == 0)
+    d.rb = r0;
+  else
+    d.rb = ka->rbs[rbi];
   return d;
 }
 
@@ -651,9 +684,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(
                 "LDS");
   static_assert(PAIRS * 64 * sizeof(f32x4) <= sizeof(ring.ring[0]), "accumulator dump");
   constexpr int DMA_PER_BLOCK = 2 * (32 * D / 1024 + 1);
-  const int w = swizzled_block();
-  if (w >= a.total_wgs) return;
+  const int w = swizzled_block(a.total_wgs);
+  // (the mapping's reads do not depend on w being in range; leaving first)
   const DecodeWork dw = decode_work(a, w);
+  if (w >= a.total_wgs) return;
   const DecodeGroup& g = dw.g;
   const RowBlock& rb = dw.rb;
   const int seq = dw.seq, chunk = dw.chunk;
@@ -958,7 +992,7 @@ __global__ __launch_bounds__(kAppendWaves * 64) void append_kernel(
   constexpr int KIB = AppendGeo<D>::KIB, PIECES = AppendGeo<D>::PIECES;
   constexpr int MY_PIECES_MAX = (PIECES + W - 1) / W;
   __shared__ AppendLds<D, W, RB> sm;
-  const int w = swizzled_block();
+  const int w = swizzled_block(a.total_wgs);
   if (w >= a.total_wgs) return;
   uint32_t q_, r_;
   udiv_recip((uint32_t)w, (uint32_t)a.token_blocks, a.tb_recip, q_, r_);
@@ -970,9 +1004,10 @@ __global__ __launch_bounds__(kAppendWaves * 64) void append_kernel(
   udiv_recip(q_, (uint32_t)a.num_layers, a.layer_recip, q_, r_);
   const int oi = (int)r_;
   const int seq = (int)q_;
-  const int layer = a.order[oi];
-  const int slot = a.layer_slot[layer];
-  const int window = a.layer_window[layer];
+  const AppendArgs* ka = first_kernel_arg<AppendArgs>();
+  const int layer = ka->order[oi];
+  const int slot = ka->layer_slot[layer];
+  const int window = ka->layer_window[layer];
 
   const int lane = lane_id(), li = lane & 15, lg = lane >> 4;
   const int wv = threadIdx.x >> 6;
