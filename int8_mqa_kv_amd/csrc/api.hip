@@ -116,15 +116,40 @@ int target_workgroups() {
   return v;
 }
 
+// MQA_DECODE_ROWS = 8, 16 or 32 forces the query rows per row block (a
+// tuning aid, like MQA_DECODE_TARGET_WGS); 0 when unset.
+int decode_rows_override() {
+  static const int v = [] {
+    const char* e = getenv("MQA_DECODE_ROWS");
+    const int t = e ? atoi(e) : 0;
+    return (t == 8 || t == 16 || t == 32) ? t : 0;
+  }();
+  return v;
+}
+
+// Query rows per row block.  32 rows (two 16-row tiles per wavefront) read
+// each page once for the most rows and cost the least vector work per (row,
+// key).  When every sequence's key range is short (at most 128 pages: the
+// 1024-token window, short contexts), a launch is bound by latency instead:
+// its keys are split into few chunks whose partial results must be handed
+// between workgroups.  There, 16-row blocks double the workgroups per page
+// (the second reads the pages from L2), halve the chunks each range needs and
+// the size of every partial record, and shorten the handoff.
+int decode_rows(int num_q_heads, int num_layers, int64_t max_span_pages, int64_t items32) {
+  int rows = decode_rows_override();
+  if (rows == 0)
+    rows = (num_q_heads > 16 && max_span_pages <= 128 && 2 * items32 <= target_workgroups())
+               ? 16 : kRowsPerBlock;
+  if (num_layers * ((num_q_heads + rows - 1) / rows) > kMaxRowBlocks) rows = kRowsPerBlock;
+  return rows;
+}
+
 DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
                        const int32_t* layer_slot, const int32_t* layer_window,
                        int32_t max_context, int32_t head_dim) {
   DecodePlan p;
   DecodeArgs& a = p.args;
   memset(&a, 0, sizeof a);
-  p.nrt = num_q_heads <= 16 ? 1 : 2;
-  const int head_blocks = (num_q_heads + kRowsPerBlock - 1) / kRowsPerBlock;
-
   // groups of layers reading one slot with one window, in first-seen order
   std::vector<std::pair<int, int>> keys;
   std::vector<std::vector<int>> members;
@@ -143,22 +168,32 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
                 (int)keys.size(), kMaxGroups);
     return p;
   }
-  if (num_layers * head_blocks > kMaxRowBlocks) {
-    p.rc = fail(MQA_ERR_UNSUPPORTED, "%d row blocks (layers x ceil(heads/32)) in one call; at most %d",
-                num_layers * head_blocks, kMaxRowBlocks);
-    return p;
-  }
 
   // Pages a sequence can span in each group (a window that does not start on
-  // a page boundary touches one page more), and the work of all items, an
-  // item being one row block of one sequence.
+  // a page boundary touches one page more).
   const int64_t ctx_pages = (max_context + kPageTokens - 1) / kPageTokens;
   std::vector<int64_t> max_np(keys.size());
-  int64_t items = 0, work = 0;
+  int64_t span = 0;
   for (size_t g = 0; g < keys.size(); ++g) {
     const int w = keys[g].second;
     max_np[g] = w > 0 ? std::min<int64_t>((w + kPageTokens - 1) / kPageTokens + 1, ctx_pages)
                       : ctx_pages;
+    span = std::max(span, max_np[g]);
+  }
+  const int64_t items32 =
+      (int64_t)num_layers * ((num_q_heads + kRowsPerBlock - 1) / kRowsPerBlock) * batch;
+  const int rows = decode_rows(num_q_heads, num_layers, span, items32);
+  p.nrt = std::min(rows, (int)num_q_heads) <= 16 ? 1 : 2;
+  const int head_blocks = (num_q_heads + rows - 1) / rows;
+  if (num_layers * head_blocks > kMaxRowBlocks) {
+    p.rc = fail(MQA_ERR_UNSUPPORTED, "%d row blocks (layers x ceil(heads/%d)) in one call; at most %d",
+                num_layers * head_blocks, rows, kMaxRowBlocks);
+    return p;
+  }
+
+  // The work of all items, an item being one row block of one sequence.
+  int64_t items = 0, work = 0;
+  for (size_t g = 0; g < keys.size(); ++g) {
     const int64_t n = (int64_t)members[g].size() * head_blocks * batch;
     items += n;
     work += n * max_np[g];
@@ -190,8 +225,8 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
     for (int l : members[g])
       for (int hb = 0; hb < head_blocks; ++hb) {
         a.rbs[rb].layer = l;
-        a.rbs[rb].head0 = hb * kRowsPerBlock;
-        a.rbs[rb].nrows = std::min(kRowsPerBlock, num_q_heads - hb * kRowsPerBlock);
+        a.rbs[rb].head0 = hb * rows;
+        a.rbs[rb].nrows = std::min(rows, num_q_heads - hb * rows);
         ++rb;
       }
     G.num_rb = rb - G.first_rb;

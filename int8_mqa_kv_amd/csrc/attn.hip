@@ -170,6 +170,7 @@ __device__ __forceinline__ void convert_q(QOps<D, QS, NRT>& o, const QRaw<D, QS,
 template <int D, int NRT>
 struct WaveState {
   f32x4 acc[NRT][Geo<D>::VT];  // O^T tiles: lane (i, g) holds channels 16t+4g..+3 of row i
+  f32x4 psum[NRT];             // sum of the P operand over keys, row i (all 4 equal)
   float m[NRT];                // running max (log2 domain), equal on a row's 4 lanes
   float l[NRT];                // this lane's part of the row's running sum
   int ev;                      // exponent of the largest V scale seen (kNoExp: none)
@@ -179,10 +180,21 @@ struct WaveState {
     for (int n = 0; n < NRT; ++n) {
       m[n] = kNegInf;
       l[n] = 0.0f;
+      psum[n] = f32x4{0, 0, 0, 0};
 #pragma unroll
       for (int t = 0; t < Geo<D>::VT; ++t) acc[n][t] = f32x4{0, 0, 0, 0};
     }
     ev = kNoExp;
+  }
+  // The accumulators hold P.(V codes + kVBias): remove kVBias * sum(P).
+  __device__ __forceinline__ void unbias() {
+#pragma unroll
+    for (int n = 0; n < NRT; ++n)
+#pragma unroll
+      for (int t = 0; t < Geo<D>::VT; ++t)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          acc[n][t][k] = __builtin_fmaf(-kVBias, psum[n][k], acc[n][t][k]);
   }
 };
 
@@ -295,19 +307,27 @@ __device__ __forceinline__ void attend_block(WaveState<D, NRT>& st, const QOps<D
       const float f = ldexp2(alpha[n], dexp);
 #pragma unroll
       for (int t = 0; t < Geo<D>::VT; ++t) st.acc[n][t] *= f;
+      st.psum[n] *= f;
     }
   }
 
+  // V codes enter as c + kVBias (two byte permutes per four codes); the
+  // matching sum of P comes from one more product with an all-ones operand,
+  // so it uses the very fp16 P values the accumulators saw.
 #pragma unroll
   for (int t = 0; t < Geo<D>::VT; ++t) {
     const int h = t >> 2, dw = t & 3;
     f16x2 a0, a1, b0, b1;
-    i8x4_to_f16x4(p0.v[h][dw], a0, a1);
-    i8x4_to_f16x4(p1.v[h][dw], b0, b1);
+    i8x4_to_f16x4_biased(p0.v[h][dw], a0, a1);
+    i8x4_to_f16x4_biased(p1.v[h][dw], b0, b1);
     const f16x8 vop = {a0[0], a0[1], a1[0], a1[1], b0[0], b0[1], b1[0], b1[1]};
 #pragma unroll
     for (int n = 0; n < NRT; ++n) st.acc[n][t] = mma16(vop, pop[n], st.acc[n][t]);
   }
+  const _Float16 one = 1.0f;
+  const f16x8 ones = {one, one, one, one, one, one, one, one};
+#pragma unroll
+  for (int n = 0; n < NRT; ++n) st.psum[n] = mma16(ones, pop[n], st.psum[n]);
 }
 
 template <int D, int QS, int NRT>
@@ -748,6 +768,23 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(
   __builtin_amdgcn_sched_barrier(0);
   sq.store(sm, stage, rb.nrows, a.scale_log2, wv, lane);
   __builtin_amdgcn_sched_barrier(0);
+  const int tok = (hi - 1) & 15;  // the current token's place in page p_last
+  // the block of this wavefront holding page p_last (the range's last), or -1
+  const int b_cur = p_last >= pbeg && p_last < pend ? (p_last - pbeg) >> 1 : -1;
+  if constexpr (NK != NewKV::kNone) {
+    // The wavefront whose pages include p_last codes the current token now.
+    // The one workgroup per slot and sequence that keeps it for later steps
+    // stores it here, so that the store flies with the first page loads
+    // instead of being waited for after the last one.  Every reader of the
+    // page, this one included, writes the token into its LDS copy, so loads
+    // of that page need not see the store.
+    if (b_cur >= 0) {
+      cur.code();
+      int pid;
+      if (g.writes_new_kv && dw.rbl == 0 && page_ok(p_last, pid))
+        cur.put(pool + (int64_t)pid * page_bytes(D), tok, lane);
+    }
+  }
   // branch-free: a page that is out of range or has a bad id loads page 0
   // instead (it exists) and is masked later
   auto issue_block = [&](int pa, int slot0) {
@@ -775,7 +812,6 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(
       for (int h = 0; h < D / 64; ++h) q.q8[n][hl][h] = sm.q8[n][hl][h][lane];
   }
 
-  const int tok = (hi - 1) & 15;  // the current token's place in page p_last
   WaveState<D, NRT> st;
   st.init();
   for (int b = 0; b < nblk; ++b) {
@@ -787,10 +823,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((RB - 2) * DMA_PER_BLOCK));
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (NK != NewKV::kNone) {
-      if (pa == p_last || pa + 1 == p_last) {  // wave-uniform: the one wavefront holding it
-        cur.code();
+      if (b == b_cur)  // the one wavefront holding the current token (coded above)
         cur.put(ring.ring[wv][cs + (p_last - pa)], tok, lane);
-      }
     }
     PageRegs<D> c0, c1;
     lds_page<D>(c0, ring.ring[wv][cs], lane, lg);
@@ -803,14 +837,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(
     if (RB > 2 || b + 1 < nblk) issue_block(pa + 2 * (RB - 1), 2 * ((b + RB - 1) % RB));
     attend_block_any<D, QS, NRT>(st, q, c0, c1, ok0, ok1, pa * kPageTokens, lo, hi, lg);
   }
-  if constexpr (NK != NewKV::kNone) {
-    // one workgroup per slot and sequence keeps the token for later steps
-    if (g.writes_new_kv && dw.rbl == 0 && p_last >= pbeg && p_last < pend) {
-      int pid;
-      if (page_ok(p_last, pid)) cur.put(pool + (int64_t)pid * page_bytes(D), tok, lane);
-    }
-  }
 
+  st.unbias();
   // ---- merge the W wavefronts: one LDS exchange ----
   // Every page load into this wavefront's ring has landed, so the wavefront
   // can dump its accumulators into its own ring without waiting for others.
@@ -1119,6 +1147,7 @@ __global__ __launch_bounds__(kAppendWaves * 64) void append_kernel(
   // every load of this wavefront has landed before the workgroup exits
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   if (!live) return;
+  st.unbias();
 #pragma unroll
   for (int n = 0; n < NRT; ++n) {
     const int row = 16 * n + li;

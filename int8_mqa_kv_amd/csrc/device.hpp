@@ -42,6 +42,16 @@ __device__ __forceinline__ void i8x4_to_f16x4(uint32_t w, f16x2& lo, f16x2& hi) 
   hi = bitcast<f16x2>(b) - bias;
 }
 
+// The same four codes as fp16 values c + kVBias (1152 + c, exact), without the
+// subtraction: a product of these with P carries kVBias * sum(P), which the
+// caller removes once, from the same P summed on the matrix cores.
+constexpr float kVBias = 1152.0f;
+__device__ __forceinline__ void i8x4_to_f16x4_biased(uint32_t w, f16x2& lo, f16x2& hi) {
+  const uint32_t u = w ^ 0x80808080u;
+  lo = bitcast<f16x2>(__builtin_amdgcn_perm(0x64646464u, u, 0x04010400u));
+  hi = bitcast<f16x2>(__builtin_amdgcn_perm(0x64646464u, u, 0x04030402u));
+}
+
 // Eight codes in two dwords -> one f16x8 operand (element k = byte k).
 __device__ __forceinline__ f16x8 i8x8_to_f16x8(uint32_t w0, uint32_t w1) {
   f16x2 a, b, c, d;
@@ -87,15 +97,23 @@ __device__ __forceinline__ void q15_pack4(uint32_t t0, uint32_t t1, uint32_t t2,
 // the gfx950 lane swaps: permlane16_swap(x, x) returns {x[l], x[l^16]} in some
 // order on every lane (permlane32_swap likewise for l^32), so one swap and one
 // max or add combine a lane with its partner without going through LDS.
+// The larger of two floats as one v_max_f32.  fmaxf on values fresh from a
+// lane swap first quiets each operand with a v_max_f32 of its own (IEEE mode
+// requires it for signalling NaNs, and no operand here is one).
+__device__ __forceinline__ float max2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ __forceinline__ float xor16_max(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(bitcast<uint32_t>(x), bitcast<uint32_t>(x), false,
                                                   false);
-  return fmaxf(bitcast<float>((uint32_t)r[0]), bitcast<float>((uint32_t)r[1]));
+  return max2(bitcast<float>((uint32_t)r[0]), bitcast<float>((uint32_t)r[1]));
 }
 __device__ __forceinline__ float xor32_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(bitcast<uint32_t>(x), bitcast<uint32_t>(x), false,
                                                   false);
-  return fmaxf(bitcast<float>((uint32_t)r[0]), bitcast<float>((uint32_t)r[1]));
+  return max2(bitcast<float>((uint32_t)r[0]), bitcast<float>((uint32_t)r[1]));
 }
 __device__ __forceinline__ float xor16_add(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(bitcast<uint32_t>(x), bitcast<uint32_t>(x), false,
