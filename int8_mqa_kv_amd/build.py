@@ -5,7 +5,9 @@
 Each ``csrc/*.hip`` file is compiled by hipcc for ``--offload-arch=gfx950``
 and linked into ``libmqa_kv.so`` beside this file.  Packed-fp32 instructions
 are disabled (``-packed-fp32-ops``); the build then checks the device assembly
-and refuses a library that contains any packed-fp32 arithmetic.
+and refuses a library that contains any packed-fp32 arithmetic, or a kernel
+that keeps anything in per-lane scratch memory (arrays the compiler could not
+hold in registers: every kernel here is meant to live in registers and LDS).
 """
 import concurrent.futures
 import glob
@@ -25,6 +27,18 @@ FLAGS = [
     "-Wno-unused-function", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 PACKED_FP32 = re.compile(r"\bv_pk_(add|mul|fma)_f32\b")
+KERNEL_META = re.compile(r"\.name:\s+(\S+)")
+SCRATCH = re.compile(r"\.private_segment_fixed_size:\s+(\d+)")
+
+
+def _scratch_kernels(text):
+    """(kernel, bytes) for every kernel of an assembly file with a private segment."""
+    out = []
+    for block in text.split("  - .agpr_count:")[1:]:
+        name, size = KERNEL_META.search(block), SCRATCH.search(block)
+        if name and size and int(size.group(1)) > 0:
+            out.append((name.group(1), int(size.group(1))))
+    return out
 
 
 def _run(cmd, verbose):
@@ -46,6 +60,9 @@ def _compile(src, objdir, verbose):
     bad = sorted(set(m.group(0) for m in PACKED_FP32.finditer(text)))
     if bad:
         raise RuntimeError(f"{src}: packed-fp32 instructions in device code: {bad}")
+    scratch = _scratch_kernels(text)
+    if scratch:
+        raise RuntimeError(f"{src}: kernels using scratch memory: {scratch}")
     return obj
 
 

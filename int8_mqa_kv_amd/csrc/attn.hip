@@ -939,7 +939,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(
 
   // ---- this wavefront's pairs over all chunks, folded in chunk order ----
   // (the order, not the arrival, fixes the rounding: results are deterministic)
-  constexpr int CB = 8;  // records loaded per round trip
+  // Records are loaded only for chunks that exist, CB per round trip; this
+  // wavefront's own chunk comes from its registers (the same values).
+  constexpr int CB = 8;
   float M[PPW], L[PPW];
   f32x4 A[PPW];
 #pragma unroll
@@ -952,11 +954,19 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(
     float mc[PPW][CB], lc[PPW][CB];
     f32x4 ac[PPW][CB];
 #pragma unroll
-    for (int k = 0; k < PPW; ++k) {
-      const int pi = min(wv + k * W, PAIRS - 1);
+    for (int u = 0; u < CB; ++u) {
+      const int c = c0 + u;
+      if (c >= nch) break;  // wave-uniform
 #pragma unroll
-      for (int u = 0; u < CB; ++u) {
-        const float* r = recs + (rec0 + min(c0 + u, nch - 1)) * RS + pi * PF;
+      for (int k = 0; k < PPW; ++k) {
+        if (c == chunk) {
+          mc[k][u] = Mr[k];
+          lc[k][u] = Lr[k];
+          ac[k][u] = Ar[k];
+          continue;
+        }
+        const int pi = min(wv + k * W, PAIRS - 1);
+        const float* r = recs + (rec0 + c) * RS + pi * PF;
         mc[k][u] = ld_dev(r + li);
         lc[k][u] = ld_dev(r + 16 + li);
 #pragma unroll
