@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MQA_KV_ABI_VERSION 2
+#define MQA_KV_ABI_VERSION 3
 #define MQA_PAGE_TOKENS 16
 
 typedef enum {
@@ -263,6 +263,86 @@ int mqa_append_attn(const void* q, mqa_dtype q_dtype, float* out,
                     int32_t num_q_heads, int32_t num_layers, int32_t num_slots,
                     const int32_t* layer_slot, const int32_t* layer_window,
                     float softmax_scale, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Host-side memory management of the paged cache.  Nothing below launches
+ * work or touches device memory; every pointer is a HOST pointer.
+ * ------------------------------------------------------------------------- */
+
+/*
+ * Bytes of KV cache one sequence holds at `context` tokens (its positions
+ * 0 .. context-1), for a model whose layer l reads slot layer_slot[l] through
+ * window layer_window[l] (0 = global).  The techniques of "Character.AI:
+ * inference optimization", section 03, technique table, each show up here:
+ *  - multi-query attention: num_kv_heads = 1 (grouped-query: 8);
+ *  - KV shared across layers: each distinct slot is stored once;
+ *  - hybrid local/global attention: a slot that only windowed layers read
+ *    keeps only the tokens its widest window still reaches,
+ *    max(0, context - W) .. context-1 (see mqa_page_table_advance);
+ * and section 05 (int8 KV cache) through code_bytes = 1 and scale_bytes = 4
+ * (one fp32 scale per token, KV head and K or V); bf16: 2 and 0.
+ * Per token and slot: 2 x num_kv_heads x (head_dim x code_bytes +
+ * scale_bytes), which with one slot per layer and no scales is the formula of
+ * "Como funciona a inferência de IA", section "Qual é o tamanho real do cache
+ * KV?".  page_tokens > 0 counts whole pages of that many tokens (what a paged
+ * pool holds: MQA_PAGE_TOKENS for this library); 0 counts tokens exactly.
+ * Returns -1 for a negative argument or a NULL map with num_layers > 0.
+ */
+int64_t mqa_kv_footprint_bytes(int32_t num_layers, const int32_t* layer_slot,
+                               const int32_t* layer_window, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t code_bytes, int32_t scale_bytes,
+                               int64_t context, int32_t page_tokens);
+
+/*
+ * Page table with recycling of windowed slots: a host object that hands out
+ * the pool pages first_page .. first_page+num_pages-1 to (slot, sequence)
+ * pairs as sequences grow, and takes back every page of a windowed slot once
+ * no later step can read it (all its tokens lie before the window of the
+ * sequence's earliest remaining query).  Pages are fixed-size blocks placed
+ * anywhere, found through a per-request table ("Como funciona a inferência
+ * de IA", section "O que os servidores ... fazem a respeito?", item 1); the
+ * local layers' horizon ("Character.AI: inference optimization", section 03)
+ * bounds what a local slot must keep to ceil(W/16) + 1 pages for decode
+ * steps.  The object writes the rows of the caller's host block table
+ * ([num_slots][batch][max_pages] int32, the layout mqa_decode_attn reads once
+ * copied to the device); entries of pages not held are `invalid_page` (a
+ * value outside the managed range: -1, or a poison page of the caller's).
+ * Not thread-safe: one object per host thread or external locking.
+ *
+ * create:   slot_window[num_slots] (0 = global).  *out receives the object;
+ *           destroy frees it.
+ * advance:  sequence `seq` now holds `context` tokens, the last `new_tokens`
+ *           of which form this step's queries (1 for a decode step, the
+ *           chunk length for mqa_append_attn).  Frees the pages of windowed
+ *           slots that fall entirely before max(0, context - new_tokens + 1 -
+ *           W), then gives the sequence pages up to token context-1 in every
+ *           slot.  The sequence's first call writes its whole row of each
+ *           slot in block_table; later calls write only the entries they
+ *           change (block_table may be NULL to keep no mirror).  Errors
+ *           (nothing changes): context below the sequence's, beyond
+ *           max_pages x 16, new_tokens outside [1, context], an earliest
+ *           query before the last step's (MQA_ERR_INVALID); the free list
+ *           too short (MQA_ERR_UNSUPPORTED).
+ * release:  the sequence ends: all its pages go back; its rows become
+ *           invalid_page.
+ * free_pages / held_pages: free-list length; pages (seq, slot) holds (-1 on
+ *           a bad argument).
+ * slot_mapping: page*16 + offset of tokens start .. start+count-1 of (seq,
+ *           slot), the form kv_pack_int8 takes; MQA_ERR_INVALID if one of
+ *           them has no page.
+ */
+typedef struct mqa_page_table mqa_page_table;
+int mqa_page_table_create(int32_t first_page, int32_t num_pages, int32_t num_slots,
+                          const int32_t* slot_window, int32_t batch, int32_t max_pages,
+                          int32_t invalid_page, mqa_page_table** out);
+int mqa_page_table_destroy(mqa_page_table* table);
+int mqa_page_table_advance(mqa_page_table* table, int32_t seq, int64_t context,
+                           int32_t new_tokens, int32_t* block_table);
+int mqa_page_table_release(mqa_page_table* table, int32_t seq, int32_t* block_table);
+int64_t mqa_page_table_free_pages(const mqa_page_table* table);
+int64_t mqa_page_table_held_pages(const mqa_page_table* table, int32_t seq, int32_t slot);
+int mqa_page_table_slot_mapping(const mqa_page_table* table, int32_t seq, int32_t slot,
+                                int64_t start, int32_t count, int64_t* out);
 
 #ifdef __cplusplus
 }

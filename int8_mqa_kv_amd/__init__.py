@@ -77,6 +77,20 @@ def _load() -> ctypes.CDLL:
     L.mqa_append_attn.argtypes = [p, ctypes.c_int, p, ctypes.POINTER(_Pool), p, i32, p, p, i32,
                                   i32, i32, i32, i32, i32, i32, p, p, f32, p]
     L.mqa_append_attn.restype = ctypes.c_int
+    L.mqa_kv_footprint_bytes.argtypes = [i32, p, p, i32, i32, i32, i32, i64, i32]
+    L.mqa_kv_footprint_bytes.restype = i64
+    L.mqa_page_table_create.argtypes = [i32, i32, i32, p, i32, i32, i32, ctypes.POINTER(p)]
+    L.mqa_page_table_create.restype = ctypes.c_int
+    L.mqa_page_table_destroy.argtypes, L.mqa_page_table_destroy.restype = [p], ctypes.c_int
+    L.mqa_page_table_advance.argtypes = [p, i32, i64, i32, p]
+    L.mqa_page_table_advance.restype = ctypes.c_int
+    L.mqa_page_table_release.argtypes = [p, i32, p]
+    L.mqa_page_table_release.restype = ctypes.c_int
+    L.mqa_page_table_free_pages.argtypes, L.mqa_page_table_free_pages.restype = [p], i64
+    L.mqa_page_table_held_pages.argtypes = [p, i32, i32]
+    L.mqa_page_table_held_pages.restype = i64
+    L.mqa_page_table_slot_mapping.argtypes = [p, i32, i32, i64, i32, p]
+    L.mqa_page_table_slot_mapping.restype = ctypes.c_int
     return L
 
 
@@ -97,6 +111,68 @@ def page_bytes(head_dim: int) -> int:
 
 def kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int, dtype_bytes: int) -> int:
     return int(lib.mqa_kv_bytes_per_token(num_layers, num_kv_heads, head_dim, dtype_bytes))
+
+
+def kv_footprint_bytes(layer_slot: Sequence[int], layer_window: Sequence[int], num_kv_heads: int,
+                       head_dim: int, code_bytes: int, scale_bytes: int, context: int,
+                       page_tokens: int = PAGE_TOKENS) -> int:
+    """KV bytes one sequence holds at ``context`` tokens for a layer map
+    (``mqa_kv_footprint_bytes``)."""
+    n = len(layer_slot)
+    ls = _host_i32(layer_slot, n, "layer_slot")
+    lw = _host_i32(layer_window, n, "layer_window")
+    r = int(lib.mqa_kv_footprint_bytes(n, ls.ctypes.data, lw.ctypes.data, num_kv_heads, head_dim,
+                                       code_bytes, scale_bytes, int(context), page_tokens))
+    if r < 0:
+        raise MQAError(MQA_ERR_INVALID, "invalid footprint arguments")
+    return r
+
+
+class PageTable:
+    """Page table with recycling of windowed slots (``mqa_page_table_*``).
+    ``block_table`` is the host mirror ([num_slots, batch, max_pages] int32)
+    the library writes; copy it to the device for the attention calls."""
+
+    def __init__(self, first_page: int, num_pages: int, slot_window: Sequence[int], batch: int,
+                 max_pages: int, invalid_page: int = -1):
+        self.num_slots = len(slot_window)
+        self.batch, self.max_pages = batch, max_pages
+        sw = _host_i32(slot_window, self.num_slots, "slot_window")
+        h = ctypes.c_void_p()
+        _check(lib.mqa_page_table_create(first_page, num_pages, self.num_slots, sw.ctypes.data,
+                                         batch, max_pages, invalid_page, ctypes.byref(h)))
+        self._h = h
+        self.block_table = np.full((self.num_slots, batch, max_pages), invalid_page, np.int32)
+
+    def close(self) -> None:
+        if self._h is not None and self._h.value:
+            lib.mqa_page_table_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def advance(self, seq: int, context: int, new_tokens: int = 1) -> None:
+        _check(lib.mqa_page_table_advance(self._h, seq, int(context), int(new_tokens),
+                                          self.block_table.ctypes.data))
+
+    def release(self, seq: int) -> None:
+        _check(lib.mqa_page_table_release(self._h, seq, self.block_table.ctypes.data))
+
+    def free_pages(self) -> int:
+        return int(lib.mqa_page_table_free_pages(self._h))
+
+    def held_pages(self, seq: int, slot: int) -> int:
+        return int(lib.mqa_page_table_held_pages(self._h, seq, slot))
+
+    def slot_mapping(self, seq: int, slot: int, start: int, count: int) -> np.ndarray:
+        out = np.empty(count, np.int64)
+        _check(lib.mqa_page_table_slot_mapping(self._h, seq, slot, int(start), int(count),
+                                               out.ctypes.data))
+        return out
 
 
 _layout_cache = {}

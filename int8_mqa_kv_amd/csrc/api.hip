@@ -15,7 +15,7 @@
 
 using namespace mqa;
 
-namespace {
+namespace mqa {
 
 thread_local std::string g_last_error;
 
@@ -33,6 +33,10 @@ int ok() {
   g_last_error.clear();
   return MQA_OK;
 }
+
+}  // namespace mqa
+
+namespace {
 
 int hip_fail(hipError_t e, const char* what) {
   return fail(MQA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));

@@ -102,6 +102,11 @@ struct AppendPtrs {
   const int32_t* cu_q_lens;
 };
 
+// Status reporting shared by the C entry points: fail() records the message
+// mqa_last_error() returns and passes the status code through; ok() clears it.
+int fail(int code, const char* fmt, ...);
+int ok();
+
 hipError_t launch_pack(int D, bool bf16, const void* k, const void* v, int64_t num_tokens,
                        int64_t row_stride, const int64_t* slot_mapping, uint8_t* pool,
                        int64_t num_pages, hipStream_t stream);

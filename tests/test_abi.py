@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_sizes():
-    assert mk.lib.mqa_abi_version() == 2
+    assert mk.lib.mqa_abi_version() == 3
     assert mk.page_bytes(128) == 32 * 128 + 128 == 4224
     assert mk.page_bytes(64) == 2176
     assert mk.lib.mqa_page_bytes(96) == 0
