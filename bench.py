@@ -387,10 +387,51 @@ def main():
                       "HIP graph replay of back-to-back calls, events around the replays")
     roof["traffic"] = traffic_from_profile(w.case, kv_bytes)
     res["roofline"] = roof
+    res["memory"] = memory_report(w, mk)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host cores ...")
         res["cpu_baseline"] = cpu_baseline(w, kv_bytes, args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def memory_report(w, mk, steps=200):
+    """KV bytes one sequence of the workload holds at its longest context:
+    int8 pages with windowed slots recycled (mqa_kv_footprint_bytes), the same
+    cache without recycling, and a bf16 grouped-query cache (8 KV heads) with
+    every layer global and its own slot; plus the host time the page table
+    (mqa_page_table_advance) takes for one decode step of the whole batch."""
+    ls, lw = w.layer_slot.tolist(), w.layer_window.tolist()
+    L, ctx = len(ls), int(w.max_context)
+    held = mk.kv_footprint_bytes(ls, lw, 1, w.head_dim, 1, 4, ctx)
+    no_recycle = mk.kv_footprint_bytes(ls, [0] * L, 1, w.head_dim, 1, 4, ctx)
+    gqa = mk.kv_footprint_bytes(list(range(L)), [0] * L, 8, w.head_dim, 2, 0, ctx, 0)
+    slot_window = [0] * w.num_slots
+    for s_, win in zip(ls, lw):
+        slot_window[s_] = win if slot_window[s_] == 0 and win > 0 else slot_window[s_]
+    for s_, win in zip(ls, lw):
+        if win == 0:
+            slot_window[s_] = 0
+    max_pages = (ctx + steps + 15) // 16
+    pages = w.batch * w.num_slots * max_pages
+    pt = mk.PageTable(0, pages, slot_window, w.batch, max_pages)
+    start = [int(c) for c in w.context_lens]
+    for b, c in enumerate(start):
+        pt.advance(b, c, c)
+    ctx_now = np.array(start, np.int64)
+    ones = np.ones(w.batch, np.int32)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        ctx_now += 1
+        pt.advance_all(ctx_now, ones)
+    dt = (time.perf_counter() - t0) / steps
+    pt.close()
+    return {"context": ctx, "kv_bytes_held_per_seq": held,
+            "without_recycling": no_recycle,
+            "recycling_factor": round(no_recycle / held, 3),
+            "vs_gqa8_bf16_every_layer_global": round(gqa / held, 2),
+            "page_table_us_per_step": round(dt * 1e6, 1),
+            "page_table_timing": f"one mqa_page_table_advance_all call (a decode step of the "
+                                 f"{w.batch} sequences) from Python, mean of {steps} steps"}
 
 
 def counters_path(case):

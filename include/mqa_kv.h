@@ -323,6 +323,10 @@ int64_t mqa_kv_footprint_bytes(int32_t num_layers, const int32_t* layer_slot,
  *           max_pages x 16, new_tokens outside [1, context], an earliest
  *           query before the last step's (MQA_ERR_INVALID); the free list
  *           too short (MQA_ERR_UNSUPPORTED).
+ * advance_all: one step of the whole batch in one call: context[batch] and
+ *           new_tokens[batch] (host) as for advance, new_tokens[b] = 0 for a
+ *           sequence that does not step.  All or nothing: on any error no
+ *           sequence changes.  Every stepping sequence frees before any grows.
  * release:  the sequence ends: all its pages go back; its rows become
  *           invalid_page.
  * free_pages / held_pages: free-list length; pages (seq, slot) holds (-1 on
@@ -338,6 +342,8 @@ int mqa_page_table_create(int32_t first_page, int32_t num_pages, int32_t num_slo
 int mqa_page_table_destroy(mqa_page_table* table);
 int mqa_page_table_advance(mqa_page_table* table, int32_t seq, int64_t context,
                            int32_t new_tokens, int32_t* block_table);
+int mqa_page_table_advance_all(mqa_page_table* table, const int64_t* context,
+                               const int32_t* new_tokens, int32_t* block_table);
 int mqa_page_table_release(mqa_page_table* table, int32_t seq, int32_t* block_table);
 int64_t mqa_page_table_free_pages(const mqa_page_table* table);
 int64_t mqa_page_table_held_pages(const mqa_page_table* table, int32_t seq, int32_t slot);

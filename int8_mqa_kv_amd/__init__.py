@@ -84,6 +84,8 @@ def _load() -> ctypes.CDLL:
     L.mqa_page_table_destroy.argtypes, L.mqa_page_table_destroy.restype = [p], ctypes.c_int
     L.mqa_page_table_advance.argtypes = [p, i32, i64, i32, p]
     L.mqa_page_table_advance.restype = ctypes.c_int
+    L.mqa_page_table_advance_all.argtypes = [p, p, p, p]
+    L.mqa_page_table_advance_all.restype = ctypes.c_int
     L.mqa_page_table_release.argtypes = [p, i32, p]
     L.mqa_page_table_release.restype = ctypes.c_int
     L.mqa_page_table_free_pages.argtypes, L.mqa_page_table_free_pages.restype = [p], i64
@@ -158,6 +160,15 @@ class PageTable:
     def advance(self, seq: int, context: int, new_tokens: int = 1) -> None:
         _check(lib.mqa_page_table_advance(self._h, seq, int(context), int(new_tokens),
                                           self.block_table.ctypes.data))
+
+    def advance_all(self, context: Sequence[int], new_tokens: Sequence[int]) -> None:
+        """One step of the whole batch (``new_tokens[b] = 0``: b does not step)."""
+        c = np.ascontiguousarray(context, dtype=np.int64)
+        n = np.ascontiguousarray(new_tokens, dtype=np.int32)
+        if c.shape != (self.batch,) or n.shape != (self.batch,):
+            raise ValueError(f"context and new_tokens must have {self.batch} entries")
+        _check(lib.mqa_page_table_advance_all(self._h, c.ctypes.data, n.ctypes.data,
+                                              self.block_table.ctypes.data))
 
     def release(self, seq: int) -> None:
         _check(lib.mqa_page_table_release(self._h, seq, self.block_table.ctypes.data))

@@ -134,37 +134,45 @@ int mqa_page_table_destroy(mqa_page_table* t) {
   return ok();
 }
 
-int mqa_page_table_advance(mqa_page_table* t, int32_t seq, int64_t context, int32_t new_tokens,
-                           int32_t* block_table) {
-  if (!t) return fail(MQA_ERR_INVALID, "page table is NULL");
+}  // extern "C"
+
+namespace {
+
+// Checks of one sequence's step; MQA_OK or a status with the message set.
+int check_step(const mqa_page_table* t, int32_t seq, int64_t context, int32_t new_tokens) {
   if (seq < 0 || seq >= t->batch) return fail(MQA_ERR_INVALID, "seq %d not in [0, %d)", seq, t->batch);
   const int64_t prev = t->context[seq];
   if (context < prev)
-    return fail(MQA_ERR_INVALID, "context %lld below the sequence's %lld", (long long)context,
-                (long long)prev);
+    return fail(MQA_ERR_INVALID, "seq %d: context %lld below the sequence's %lld", seq,
+                (long long)context, (long long)prev);
   if (context > (int64_t)t->max_pages * kPage)
-    return fail(MQA_ERR_INVALID, "context %lld exceeds max_pages * 16", (long long)context);
+    return fail(MQA_ERR_INVALID, "seq %d: context %lld exceeds max_pages * 16", seq,
+                (long long)context);
   if (new_tokens < 1 || new_tokens > context)
-    return fail(MQA_ERR_INVALID, "new_tokens %d not in [1, context]", new_tokens);
+    return fail(MQA_ERR_INVALID, "seq %d: new_tokens %d not in [1, context]", seq, new_tokens);
   // pages behind a window were recycled for good: the earliest query of a
   // step may not move back before that of the sequence's last step
   if (prev > 0 && context - new_tokens < t->qfirst[seq])
-    return fail(MQA_ERR_INVALID, "earliest query %lld precedes the last step's %lld",
+    return fail(MQA_ERR_INVALID, "seq %d: earliest query %lld precedes the last step's %lld", seq,
                 (long long)(context - new_tokens), (long long)t->qfirst[seq]);
-  // count first, change nothing unless the free list covers the growth (the
-  // pages this call frees count: they serve its own new pages first)
+  return MQA_OK;
+}
+
+// Pages one sequence's step frees and takes.
+void count_step(const mqa_page_table* t, int32_t seq, int64_t context, int32_t new_tokens,
+                int64_t& to_free, int64_t& to_alloc) {
   const int64_t new_end = (context - 1) / kPage + 1;
-  int64_t to_alloc = 0, to_free = 0;
   for (int s = 0; s < t->num_slots; ++s) {
     const int64_t k = t->item(s, seq);
     const int64_t new_lo = first_readable(context, new_tokens, t->window[s]) / kPage;
     to_free += std::max<int64_t>(0, std::min(new_lo, t->end[k]) - t->lo[k]);
     to_alloc += new_end - std::max(new_lo, t->end[k]);
   }
-  if (to_alloc > (int64_t)t->free_ids.size() + to_free)
-    return fail(MQA_ERR_UNSUPPORTED, "page pool exhausted: %lld pages needed, %lld free",
-                (long long)to_alloc, (long long)(t->free_ids.size() + to_free));
-  for (int s = 0; s < t->num_slots; ++s) {  // frees first: they serve the growth
+}
+
+void free_behind(mqa_page_table* t, int32_t seq, int64_t context, int32_t new_tokens,
+                 int32_t* block_table) {
+  for (int s = 0; s < t->num_slots; ++s) {
     const int64_t k = t->item(s, seq);
     int32_t* r = t->row(s, seq);
     int32_t* out = block_table ? block_table + k * t->max_pages : nullptr;
@@ -177,6 +185,12 @@ int mqa_page_table_advance(mqa_page_table* t, int32_t seq, int64_t context, int3
     }
     t->lo[k] = std::max(t->lo[k], stop);
   }
+}
+
+void grow(mqa_page_table* t, int32_t seq, int64_t context, int32_t new_tokens,
+          int32_t* block_table) {
+  const int64_t prev = t->context[seq];
+  const int64_t new_end = (context - 1) / kPage + 1;
   for (int s = 0; s < t->num_slots; ++s) {
     const int64_t k = t->item(s, seq);
     int32_t* r = t->row(s, seq);
@@ -197,6 +211,48 @@ int mqa_page_table_advance(mqa_page_table* t, int32_t seq, int64_t context, int3
   }
   t->context[seq] = context;
   t->qfirst[seq] = context - new_tokens;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mqa_page_table_advance(mqa_page_table* t, int32_t seq, int64_t context, int32_t new_tokens,
+                           int32_t* block_table) {
+  if (!t) return fail(MQA_ERR_INVALID, "page table is NULL");
+  int rc = check_step(t, seq, context, new_tokens);
+  if (rc != MQA_OK) return rc;
+  // count first, change nothing unless the free list covers the growth (the
+  // pages this call frees count: they serve its own new pages first)
+  int64_t to_free = 0, to_alloc = 0;
+  count_step(t, seq, context, new_tokens, to_free, to_alloc);
+  if (to_alloc > (int64_t)t->free_ids.size() + to_free)
+    return fail(MQA_ERR_UNSUPPORTED, "page pool exhausted: %lld pages needed, %lld free",
+                (long long)to_alloc, (long long)(t->free_ids.size() + to_free));
+  free_behind(t, seq, context, new_tokens, block_table);
+  grow(t, seq, context, new_tokens, block_table);
+  return ok();
+}
+
+int mqa_page_table_advance_all(mqa_page_table* t, const int64_t* context,
+                               const int32_t* new_tokens, int32_t* block_table) {
+  if (!t) return fail(MQA_ERR_INVALID, "page table is NULL");
+  if (!context || !new_tokens) return fail(MQA_ERR_INVALID, "context or new_tokens is NULL");
+  int64_t to_free = 0, to_alloc = 0;
+  for (int32_t b = 0; b < t->batch; ++b) {
+    if (new_tokens[b] == 0) continue;  // not stepping
+    int rc = check_step(t, b, context[b], new_tokens[b]);
+    if (rc != MQA_OK) return rc;
+    count_step(t, b, context[b], new_tokens[b], to_free, to_alloc);
+  }
+  if (to_alloc > (int64_t)t->free_ids.size() + to_free)
+    return fail(MQA_ERR_UNSUPPORTED, "page pool exhausted: %lld pages needed, %lld free",
+                (long long)to_alloc, (long long)(t->free_ids.size() + to_free));
+  // every sequence frees before any grows: the step's frees serve its growth
+  for (int32_t b = 0; b < t->batch; ++b)
+    if (new_tokens[b] != 0) free_behind(t, b, context[b], new_tokens[b], block_table);
+  for (int32_t b = 0; b < t->batch; ++b)
+    if (new_tokens[b] != 0) grow(t, b, context[b], new_tokens[b], block_table);
   return ok();
 }
 

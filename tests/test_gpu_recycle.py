@@ -2,7 +2,7 @@
 
 Four sequences grow token by token through mqa_decode_step, with one layer
 reading a local slot (window 64) and one a global slot.  Before each step the
-page table (mqa_page_table_advance) frees the local pages that fell behind
+page table (mqa_page_table_advance_all, one call for the batch) frees the local pages that fell behind
 the window and hands out pages for the new token; the pool is too small to
 hold every page without that.  The pool starts as 0xFF bytes (NaN scales), so
 a step that read a page nobody wrote would give NaN; a step that read a
@@ -78,7 +78,8 @@ def test_decode_steps_on_recycled_pages():
         v_new = np.zeros_like(k_new)
         for b in range(batch):
             ctx[b] += 1
-            pt.advance(b, ctx[b], 1)
+        pt.advance_all(ctx, [1] * batch)          # one step of the batch
+        for b in range(batch):
             # fewer local pages than the history spans: some went back to the pool
             recycled_any |= pt.held_pages(b, 0) < -(-ctx[b] // 16)
             for s in range(2):

@@ -272,3 +272,35 @@ def test_slot_mapping_follows_the_table():
         pt.slot_mapping(1, 1, 0, 1)                 # token 0 of the windowed slot was recycled
     sm = pt.slot_mapping(1, 1, 70, 1)
     assert sm[0] == pt.block_table[1, 1, 4] * 16 + 6
+
+
+def test_advance_all_equals_one_call_per_sequence():
+    """A batch step holds the same table entries as sequence-by-sequence
+    calls (which ids: the free-list order differs, as the batch frees before
+    it grows), keeps every id unique, and is all or nothing when the pool runs
+    short."""
+    windows = [0, 48]
+    a = mk.PageTable(2, 400, windows, 5, 64, -1)
+    b = mk.PageTable(2, 400, windows, 5, 64, -1)
+    ctx = np.array([30, 1, 100, 77, 16], np.int64)
+    a.advance_all(ctx, ctx.astype(np.int32))
+    for s in range(5):
+        b.advance(s, int(ctx[s]), int(ctx[s]))
+    rng = np.random.default_rng(3)
+    for _ in range(120):
+        new = rng.integers(0, 3, size=5).astype(np.int32)
+        ctx = ctx + new
+        a.advance_all(ctx, new)
+        for s in range(5):
+            if new[s]:
+                b.advance(s, int(ctx[s]), int(new[s]))
+        assert np.array_equal(a.block_table >= 0, b.block_table >= 0)
+        ids = a.block_table[a.block_table >= 0]
+        assert ids.size == np.unique(ids).size
+        assert a.free_pages() == b.free_pages()
+    small = mk.PageTable(0, 6, [0], 2, 20, -1)
+    small.advance_all(np.array([48, 32], np.int64), np.array([48, 32], np.int32))  # 3 + 2 pages
+    before = small.block_table.copy()
+    with pytest.raises(mk.MQAError):
+        small.advance_all(np.array([49, 49], np.int64), np.array([1, 17], np.int32))  # 2 more, 1 free
+    assert np.array_equal(small.block_table, before) and small.free_pages() == 1
