@@ -388,10 +388,22 @@ def main():
     roof["traffic"] = traffic_from_profile(w.case, kv_bytes)
     res["roofline"] = roof
     res["memory"] = memory_report(w, mk)
+    if w.kind == "append":
+        log("prefix cache: offload and restore of the cached prefixes ...")
+        res["memory"]["prefix_cache"] = prefix_restore_report(w, st, mk, torch)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host cores ...")
         res["cpu_baseline"] = cpu_baseline(w, kv_bytes, args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def slot_windows(w):
+    """Per KV slot: 0 if a global layer reads it, else its widest window."""
+    out = []
+    for s_ in range(w.num_slots):
+        wins = [int(x) for x, l in zip(w.layer_window, w.layer_slot) if int(l) == s_]
+        out.append(0 if (not wins or 0 in wins) else max(wins))
+    return out
 
 
 def memory_report(w, mk, steps=200):
@@ -405,12 +417,7 @@ def memory_report(w, mk, steps=200):
     held = mk.kv_footprint_bytes(ls, lw, 1, w.head_dim, 1, 4, ctx)
     no_recycle = mk.kv_footprint_bytes(ls, [0] * L, 1, w.head_dim, 1, 4, ctx)
     gqa = mk.kv_footprint_bytes(list(range(L)), [0] * L, 8, w.head_dim, 2, 0, ctx, 0)
-    slot_window = [0] * w.num_slots
-    for s_, win in zip(ls, lw):
-        slot_window[s_] = win if slot_window[s_] == 0 and win > 0 else slot_window[s_]
-    for s_, win in zip(ls, lw):
-        if win == 0:
-            slot_window[s_] = 0
+    slot_window = slot_windows(w)
     max_pages = (ctx + steps + 15) // 16
     pages = w.batch * w.num_slots * max_pages
     pt = mk.PageTable(0, pages, slot_window, w.batch, max_pages)
@@ -432,6 +439,55 @@ def memory_report(w, mk, steps=200):
             "page_table_us_per_step": round(dt * 1e6, 1),
             "page_table_timing": f"one mqa_page_table_advance_all call (a decode step of the "
                                  f"{w.batch} sequences) from Python, mean of {steps} steps"}
+
+
+def prefix_restore_report(w, st, mk, torch):
+    """The hybrid turn starts from a cross-turn cache hit: every sequence's
+    cached prefix (context - q_len tokens) is offloaded page by page from the
+    pool into a pinned host arena (mqa_prefix_cache_insert, device -> host),
+    looked up by its token ids, and restored into the pool pages the block
+    table gives (mqa_prefix_cache_restore, host -> device).  One call per
+    sequence, timed end to end with events; token ids are seeded synthetic."""
+    R = st["reps"][0]
+    bt = np.ascontiguousarray(w.block_table)
+    slot_window = slot_windows(w)
+    prefix = (w.context_lens - w.q_lens).astype(np.int64)
+    rng = np.random.default_rng(4004)
+    tokens = [rng.integers(0, 128000, int(c)).astype(np.int32) for c in w.context_lens]
+    held = 0
+    for b in range(w.batch):
+        k = int(prefix[b]) // 16
+        rows = bt[:, b, :k]
+        held += int(np.count_nonzero((rows != w.poison_page) & (rows >= 0)))
+    entry = -(-mk.page_bytes(w.head_dim) // 256) * 256
+    pc = mk.PrefixCache(256 * 1024 + held * entry, slot_window, w.head_dim)
+    E = torch.cuda.Event
+    e0, e1, e2, e3 = (E(enable_timing=True) for _ in range(4))
+    torch.cuda.synchronize()
+    e0.record()
+    for b in range(w.batch):
+        pc.insert(tokens[b][:int(prefix[b])], R.pool, bt, b, invalid_page=w.poison_page)
+    e1.record()
+    torch.cuda.synchronize()
+    matched = [pc.lookup(tokens[b]) for b in range(w.batch)]
+    e2.record()
+    for b in range(w.batch):
+        pc.restore(tokens[b], matched[b], R.pool, bt, b, invalid_page=w.poison_page)
+    e3.record()
+    torch.cuda.synchronize()
+    st_ = pc.stats()
+    pb = mk.page_bytes(w.head_dim)
+    off_b = st_["entries_inserted"] * pb
+    res_b = st_["entries_restored"] * pb
+    out = {"entries": pc.entries(), "arena_bytes": 256 * 1024 + held * entry,
+           "offload_bytes": off_b,
+           "offload_gbs": round(off_b / (e0.elapsed_time(e1) * 1e-3) / 1e9, 2),
+           "restore_bytes": res_b,
+           "restore_gbs": round(res_b / (e2.elapsed_time(e3) * 1e-3) / 1e9, 2),
+           "matched_tokens_fraction": round(sum(matched) / float(prefix.sum()), 4),
+           "timing": f"{w.batch} calls each way (one per sequence), events around the calls"}
+    pc.close()
+    return out
 
 
 def counters_path(case):

@@ -350,6 +350,91 @@ int64_t mqa_page_table_held_pages(const mqa_page_table* table, int32_t seq, int3
 int mqa_page_table_slot_mapping(const mqa_page_table* table, int32_t seq, int32_t slot,
                                 int64_t start, int32_t count, int64_t* out);
 
+/*
+ * Cross-turn prefix cache ("Character.AI: inference optimization", section
+ * 04: the KV of earlier turns is kept in host memory in a tree-structured LRU
+ * cache indexed by a rolling hash of every prefix, and a new turn reuses the
+ * longest cached prefix; "Como funciona a inferência de IA", section "O que
+ * os servidores ... fazem a respeito?", item 3: prefix caching).
+ *
+ * A node of the tree is one page (16 tokens) of one prefix, so the tree is a
+ * radix tree over pages; it owns one arena entry per KV slot whose page it
+ * holds, byte for byte as in the pool (a windowed slot's early pages are
+ * usually recycled before a turn is offloaded, so most nodes of a long
+ * dialogue hold only the global slots).  A node is found by a 64-bit hash
+ * chained page by page over the token ids and confirmed by its parent and
+ * its 16 tokens, so a hash collision can never return another prefix.
+ * Eviction removes the least recently used leaf, so a cached page's prefix
+ * is always cached.
+ *
+ * Memory: `host_arena` is pinned host memory the caller owns (hipHostMalloc,
+ * or a pinned torch tensor), 256-byte aligned, kept alive until destroy.  The
+ * first 256 KiB hold a command ring (the copy lists the kernels read); the
+ * rest is cut into entries of mqa_page_bytes(head_dim) bytes (rounded up to
+ * 256), one per cached (page, slot): mqa_prefix_cache_capacity() of them,
+ * mqa_prefix_cache_entries() in use.  The object's own bookkeeping is host
+ * memory it allocates at create.
+ *
+ * Copies run as one kernel per 4096 pages (one wavefront per page, over the
+ * host link) enqueued on `stream`.  Calls are not thread-safe; use one
+ * stream per cache, or order the streams: an insert may evict and refill an
+ * entry that an earlier restore reads.
+ *
+ * create:  slot_window[num_slots] as for mqa_page_table_create (num_slots
+ *          <= 64).  flags = MQA_PREFIX_HOST_ONLY: no GPU is used (host
+ *          inserts and reads only; for tests and host-side loading).
+ * lookup:  the longest cached prefix of tokens[0..n) that a step whose
+ *          earliest query is the token right after it can use: a multiple of
+ *          16, at most n-1 (the last token is always left to compute as the
+ *          next query), such that every page a global slot reads and every
+ *          page of a windowed slot within its window is cached.  Marks the
+ *          pages used.  *matched receives the token count (host).
+ * restore: for pages k < matched/16 of sequence `seq` and every slot whose
+ *          entry block_table_host[slot][seq][k] is a pool page (in range and
+ *          not `invalid_page`, the table's mark for a page not held), copies
+ *          the cached page into it (host -> device).  block_table_host is the
+ *          host mirror of the step's block table ([num_slots][batch]
+ *          [max_pages]); with mqa_page_table_advance(seq, n, n - matched) it
+ *          gives exactly the pages the step reads.  MQA_ERR_INVALID (nothing
+ *          enqueued) if a needed page is not cached.
+ * insert:  the full pages of tokens[0..n) of sequence `seq`, from the pool
+ *          pages its table rows give (entries equal to `invalid_page` or out
+ *          of range: not held) (device -> host), for every page and
+ *          slot not yet cached; creates nodes as needed, evicting least
+ *          recently used leaves.  Stops early (still MQA_OK) when the arena
+ *          cannot take more or a page has no slot at all; *cached_pages
+ *          (host, may be NULL) receives how many leading pages are cached
+ *          afterwards.
+ * insert_host / read_host: the same with page bytes in host memory laid out
+ *          [page][slot][mqa_page_bytes] and a slot mask per page (present).
+ * stats:   out6 = lookups, tokens asked, tokens matched, entries inserted,
+ *          entries evicted, entries restored (an entry: one page of one slot).
+ */
+#define MQA_PREFIX_HOST_ONLY 1
+typedef struct mqa_prefix_cache mqa_prefix_cache;
+int mqa_prefix_cache_create(void* host_arena, int64_t arena_bytes, int32_t num_slots,
+                            const int32_t* slot_window, int32_t head_dim, int32_t flags,
+                            mqa_prefix_cache** out);
+int mqa_prefix_cache_destroy(mqa_prefix_cache* cache);
+int64_t mqa_prefix_cache_capacity(const mqa_prefix_cache* cache);
+int64_t mqa_prefix_cache_entries(const mqa_prefix_cache* cache);
+int mqa_prefix_cache_stats(const mqa_prefix_cache* cache, int64_t* out6);
+int mqa_prefix_cache_lookup(mqa_prefix_cache* cache, const int32_t* tokens, int64_t n,
+                            int64_t* matched);
+int mqa_prefix_cache_restore(mqa_prefix_cache* cache, const int32_t* tokens, int64_t matched,
+                             const mqa_kv_pool* pool, const int32_t* block_table_host,
+                             int32_t batch, int32_t seq, int32_t max_pages, int32_t invalid_page,
+                             void* stream);
+int mqa_prefix_cache_insert(mqa_prefix_cache* cache, const int32_t* tokens, int64_t n,
+                            const mqa_kv_pool* pool, const int32_t* block_table_host,
+                            int32_t batch, int32_t seq, int32_t max_pages, int32_t invalid_page,
+                            void* stream, int64_t* cached_pages);
+int mqa_prefix_cache_insert_host(mqa_prefix_cache* cache, const int32_t* tokens, int64_t n,
+                                 const uint8_t* pages, const uint64_t* present,
+                                 int64_t* cached_pages);
+int mqa_prefix_cache_read_host(const mqa_prefix_cache* cache, const int32_t* tokens,
+                               int64_t pages, uint8_t* out, uint64_t* present);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,6 +11,10 @@ Entry points (same names as the C ABI):
   mqa_decode_attn   one decode step over the paged int8 cache
   mqa_decode_step   kv_pack_int8 of the current token fused into mqa_decode_attn
   mqa_append_attn   causal attention of an appended chunk on a cached prefix
+Host-side memory management (no GPU work except the prefix cache's copies):
+  kv_footprint_bytes  KV bytes a sequence holds for a layer map
+  PageTable           page table recycling windowed-slot pages (mqa_page_table_*)
+  PrefixCache         cross-turn prefix cache in pinned host memory (mqa_prefix_cache_*)
 """
 from __future__ import annotations
 
@@ -30,6 +34,7 @@ __all__ = [
     "page_layout", "kv_pack_int8", "decode_workspace_bytes", "decode_workspace",
     "mqa_decode_attn", "mqa_decode_step",
     "mqa_append_attn", "slot_mapping_for", "unpack_page_tokens",
+    "kv_footprint_bytes", "PageTable", "PrefixCache",
 ]
 
 PAGE_TOKENS = 16
@@ -93,10 +98,29 @@ def _load() -> ctypes.CDLL:
     L.mqa_page_table_held_pages.restype = i64
     L.mqa_page_table_slot_mapping.argtypes = [p, i32, i32, i64, i32, p]
     L.mqa_page_table_slot_mapping.restype = ctypes.c_int
+    L.mqa_prefix_cache_create.argtypes = [p, i64, i32, p, i32, i32, ctypes.POINTER(p)]
+    L.mqa_prefix_cache_create.restype = ctypes.c_int
+    L.mqa_prefix_cache_destroy.argtypes, L.mqa_prefix_cache_destroy.restype = [p], ctypes.c_int
+    L.mqa_prefix_cache_capacity.argtypes, L.mqa_prefix_cache_capacity.restype = [p], i64
+    L.mqa_prefix_cache_entries.argtypes, L.mqa_prefix_cache_entries.restype = [p], i64
+    L.mqa_prefix_cache_stats.argtypes, L.mqa_prefix_cache_stats.restype = [p, p], ctypes.c_int
+    L.mqa_prefix_cache_lookup.argtypes = [p, p, i64, ctypes.POINTER(i64)]
+    L.mqa_prefix_cache_lookup.restype = ctypes.c_int
+    L.mqa_prefix_cache_restore.argtypes = [p, p, i64, ctypes.POINTER(_Pool), p, i32, i32, i32, i32,
+                                           p]
+    L.mqa_prefix_cache_restore.restype = ctypes.c_int
+    L.mqa_prefix_cache_insert.argtypes = [p, p, i64, ctypes.POINTER(_Pool), p, i32, i32, i32, i32,
+                                          p, ctypes.POINTER(i64)]
+    L.mqa_prefix_cache_insert.restype = ctypes.c_int
+    L.mqa_prefix_cache_insert_host.argtypes = [p, p, i64, p, p, ctypes.POINTER(i64)]
+    L.mqa_prefix_cache_insert_host.restype = ctypes.c_int
+    L.mqa_prefix_cache_read_host.argtypes = [p, p, i64, p, p]
+    L.mqa_prefix_cache_read_host.restype = ctypes.c_int
     return L
 
 
 lib = _load()
+PREFIX_HOST_ONLY = 1
 
 
 def _check(status: int) -> None:
@@ -184,6 +208,100 @@ class PageTable:
         _check(lib.mqa_page_table_slot_mapping(self._h, seq, slot, int(start), int(count),
                                                out.ctypes.data))
         return out
+
+
+class PrefixCache:
+    """Cross-turn prefix cache in pinned host memory (``mqa_prefix_cache_*``).
+
+    ``arena_bytes`` of pinned host memory are allocated through torch (or, with
+    ``host_only``, plain host memory: no GPU copies, for host-side use)."""
+
+    def __init__(self, arena_bytes: int, slot_window: Sequence[int], head_dim: int,
+                 host_only: bool = False):
+        torch = _torch()
+        self.num_slots = len(slot_window)
+        self.head_dim = head_dim
+        self.page_bytes = page_bytes(head_dim)
+        # 256 bytes of slack so that the arena can start on a 256-byte boundary
+        self.arena = torch.empty(int(arena_bytes) + 256, dtype=torch.uint8,
+                                 pin_memory=not host_only)
+        base = self.arena.data_ptr()
+        self._off = (-base) % 256
+        sw = _host_i32(slot_window, self.num_slots, "slot_window")
+        h = ctypes.c_void_p()
+        _check(lib.mqa_prefix_cache_create(base + self._off, int(arena_bytes), self.num_slots,
+                                           sw.ctypes.data, head_dim,
+                                           PREFIX_HOST_ONLY if host_only else 0, ctypes.byref(h)))
+        self._h = h
+
+    def close(self) -> None:
+        if self._h is not None and self._h.value:
+            lib.mqa_prefix_cache_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @staticmethod
+    def _tokens(tokens) -> np.ndarray:
+        return np.ascontiguousarray(tokens, dtype=np.int32)
+
+    def capacity(self) -> int:
+        return int(lib.mqa_prefix_cache_capacity(self._h))
+
+    def entries(self) -> int:
+        return int(lib.mqa_prefix_cache_entries(self._h))
+
+    def stats(self) -> dict:
+        out = np.zeros(6, np.int64)
+        _check(lib.mqa_prefix_cache_stats(self._h, out.ctypes.data))
+        keys = ("lookups", "tokens_asked", "tokens_matched", "entries_inserted",
+                "entries_evicted", "entries_restored")
+        return dict(zip(keys, (int(x) for x in out)))
+
+    def lookup(self, tokens) -> int:
+        t = self._tokens(tokens)
+        m = ctypes.c_int64()
+        _check(lib.mqa_prefix_cache_lookup(self._h, t.ctypes.data, t.size, ctypes.byref(m)))
+        return int(m.value)
+
+    def restore(self, tokens, matched: int, pool: "KVPool", block_table_host: np.ndarray, seq: int,
+                invalid_page: int = -1, stream=None) -> None:
+        t = self._tokens(tokens)
+        bt = np.ascontiguousarray(block_table_host, dtype=np.int32)
+        _check(lib.mqa_prefix_cache_restore(self._h, t.ctypes.data, int(matched),
+                                            ctypes.byref(pool.c), bt.ctypes.data, bt.shape[1], seq,
+                                            bt.shape[2], invalid_page, _stream_ptr(stream)))
+
+    def insert(self, tokens, pool: "KVPool", block_table_host: np.ndarray, seq: int,
+               invalid_page: int = -1, stream=None) -> int:
+        t = self._tokens(tokens)
+        bt = np.ascontiguousarray(block_table_host, dtype=np.int32)
+        n = ctypes.c_int64()
+        _check(lib.mqa_prefix_cache_insert(self._h, t.ctypes.data, t.size, ctypes.byref(pool.c),
+                                           bt.ctypes.data, bt.shape[1], seq, bt.shape[2],
+                                           invalid_page, _stream_ptr(stream), ctypes.byref(n)))
+        return int(n.value)
+
+    def insert_host(self, tokens, pages: np.ndarray, present: np.ndarray) -> int:
+        t = self._tokens(tokens)
+        pg = np.ascontiguousarray(pages, dtype=np.uint8)
+        pr = np.ascontiguousarray(present, dtype=np.uint64)
+        n = ctypes.c_int64()
+        _check(lib.mqa_prefix_cache_insert_host(self._h, t.ctypes.data, t.size, pg.ctypes.data,
+                                                pr.ctypes.data, ctypes.byref(n)))
+        return int(n.value)
+
+    def read_host(self, tokens, pages: int):
+        t = self._tokens(tokens)
+        out = np.empty((pages, self.num_slots, self.page_bytes), np.uint8)
+        present = np.empty(pages, np.uint64)
+        _check(lib.mqa_prefix_cache_read_host(self._h, t.ctypes.data, pages, out.ctypes.data,
+                                              present.ctypes.data))
+        return out, present
 
 
 _layout_cache = {}

@@ -44,6 +44,10 @@ int hip_fail(hipError_t e, const char* what) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+}  // namespace
+
+namespace mqa {
+
 int check_pool(const mqa_kv_pool* pool) {
   if (!pool) return fail(MQA_ERR_INVALID, "pool is NULL");
   if (pool->head_dim != 64 && pool->head_dim != 128)
@@ -55,6 +59,10 @@ int check_pool(const mqa_kv_pool* pool) {
   if (pool->reserved != 0) return fail(MQA_ERR_INVALID, "pool.reserved must be 0");
   return MQA_OK;
 }
+
+}  // namespace mqa
+
+namespace {
 
 // Shape checks common to decode and append.
 int check_attn_common(const void* q, mqa_dtype q_dtype, const float* out, const mqa_kv_pool* pool,

@@ -106,6 +106,11 @@ struct AppendPtrs {
 // mqa_last_error() returns and passes the status code through; ok() clears it.
 int fail(int code, const char* fmt, ...);
 int ok();
+}  // namespace mqa
+struct mqa_kv_pool;
+namespace mqa {
+// Checks of a pool descriptor shared by the entry points that take one.
+int check_pool(const mqa_kv_pool* pool);
 
 hipError_t launch_pack(int D, bool bf16, const void* k, const void* v, int64_t num_tokens,
                        int64_t row_stride, const int64_t* slot_mapping, uint8_t* pool,
