@@ -410,6 +410,41 @@ int mqa_page_table_slot_mapping(const mqa_page_table* table, int32_t seq, int32_
  * stats:   out6 = lookups, tokens asked, tokens matched, entries inserted,
  *          entries evicted, entries restored (an entry: one page of one slot).
  */
+/*
+ * Grouped-query bf16 decode: the baseline of "Character.AI: inference
+ * optimization", section 03, technique table (multi-query attention cuts the
+ * KV cache 8X against grouped-query attention), on the same harness, so the
+ * factor can be measured as bytes and time.  One layer; num_kv_heads K/V
+ * heads in bf16, query head j reading KV head j / (num_q_heads /
+ * num_kv_heads) (at most 16 query heads per KV head).
+ *
+ * Pool: num_pages records of mqa_gqa_page_bytes() bytes (256-byte aligned),
+ * one per 16 tokens of one sequence, holding every KV head: for head h,
+ * 64*head_dim bytes at h*64*head_dim, its 16 tokens' K then V in bf16
+ * matrix-core operand order (the order mqa_gqa_pack_bf16 writes).
+ *
+ * pack:    k, v (device) bf16 [num_tokens][num_kv_heads][head_dim];
+ *          slot_mapping int64 [num_tokens] = page*16 + position in page
+ *          (negative or past the pool: skipped).
+ * decode:  q bf16 [batch][num_q_heads][head_dim]; out fp32 same shape;
+ *          block_table int32 [batch][max_pages]; context_lens int32 [batch]
+ *          (the query at context-1); window 0 = global.  Contexts split over
+ *          workgroups use `workspace` (mqa_gqa_decode_workspace_bytes(),
+ *          no clearing needed) and a second small kernel merges them.
+ * Errors as for the other entry points.
+ */
+size_t mqa_gqa_page_bytes(int32_t num_kv_heads, int32_t head_dim);
+int mqa_gqa_pack_bf16(const void* k, const void* v, int64_t num_tokens,
+                      const int64_t* slot_mapping, void* pool, int64_t num_pages,
+                      int32_t num_kv_heads, int32_t head_dim, void* stream);
+size_t mqa_gqa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t max_context, int32_t window, int32_t head_dim);
+int mqa_gqa_decode_bf16(const void* q, float* out, const void* pool, int64_t num_pages,
+                        int32_t num_kv_heads, int32_t head_dim, const int32_t* block_table,
+                        int32_t max_pages, const int32_t* context_lens, int32_t max_context,
+                        int32_t batch, int32_t num_q_heads, int32_t window, float softmax_scale,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 #define MQA_PREFIX_HOST_ONLY 1
 typedef struct mqa_prefix_cache mqa_prefix_cache;
 int mqa_prefix_cache_create(void* host_arena, int64_t arena_bytes, int32_t num_slots,

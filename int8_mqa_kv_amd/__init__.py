@@ -15,6 +15,7 @@ Host-side memory management (no GPU work except the prefix cache's copies):
   kv_footprint_bytes  KV bytes a sequence holds for a layer map
   PageTable           page table recycling windowed-slot pages (mqa_page_table_*)
   PrefixCache         cross-turn prefix cache in pinned host memory (mqa_prefix_cache_*)
+Baseline: gqa_pack_bf16 / gqa_decode_bf16, grouped-query bf16 decode (mqa_gqa_*).
 """
 from __future__ import annotations
 
@@ -35,6 +36,7 @@ __all__ = [
     "mqa_decode_attn", "mqa_decode_step",
     "mqa_append_attn", "slot_mapping_for", "unpack_page_tokens",
     "kv_footprint_bytes", "PageTable", "PrefixCache",
+    "gqa_page_bytes", "gqa_pack_bf16", "gqa_decode_workspace", "gqa_decode_bf16",
 ]
 
 PAGE_TOKENS = 16
@@ -116,6 +118,14 @@ def _load() -> ctypes.CDLL:
     L.mqa_prefix_cache_insert_host.restype = ctypes.c_int
     L.mqa_prefix_cache_read_host.argtypes = [p, p, i64, p, p]
     L.mqa_prefix_cache_read_host.restype = ctypes.c_int
+    L.mqa_gqa_page_bytes.argtypes, L.mqa_gqa_page_bytes.restype = [i32, i32], sz
+    L.mqa_gqa_pack_bf16.argtypes = [p, p, i64, p, p, i64, i32, i32, p]
+    L.mqa_gqa_pack_bf16.restype = ctypes.c_int
+    L.mqa_gqa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.mqa_gqa_decode_workspace_bytes.restype = sz
+    L.mqa_gqa_decode_bf16.argtypes = [p, p, p, i64, i32, i32, p, i32, p, i32, i32, i32, i32, f32,
+                                      p, sz, p]
+    L.mqa_gqa_decode_bf16.restype = ctypes.c_int
     return L
 
 
@@ -302,6 +312,56 @@ class PrefixCache:
         _check(lib.mqa_prefix_cache_read_host(self._h, t.ctypes.data, pages, out.ctypes.data,
                                               present.ctypes.data))
         return out, present
+
+
+# --------------------------------------------------------------------------
+# grouped-query bf16 baseline (mqa_gqa_*)
+# --------------------------------------------------------------------------
+def gqa_page_bytes(num_kv_heads: int, head_dim: int) -> int:
+    n = int(lib.mqa_gqa_page_bytes(num_kv_heads, head_dim))
+    if n == 0:
+        raise MQAError(MQA_ERR_UNSUPPORTED, f"({num_kv_heads}, {head_dim}) unsupported")
+    return n
+
+
+def gqa_pack_bf16(k, v, slot_mapping, pool, num_kv_heads: int, stream=None) -> None:
+    """``k, v`` bf16 [T, Hkv, D]; ``pool`` a uint8 tensor [num_pages, page_bytes]."""
+    torch = _torch()
+    t, h, d = (int(x) for x in k.shape)
+    if h != num_kv_heads or tuple(v.shape) != (t, h, d):
+        raise ValueError("k and v must be [T, num_kv_heads, D]")
+    _check(lib.mqa_gqa_pack_bf16(_dev_ptr(k, "k", torch.bfloat16), _dev_ptr(v, "v", torch.bfloat16),
+                                 t, _dev_ptr(slot_mapping, "slot_mapping", torch.int64),
+                                 _dev_ptr(pool, "pool", torch.uint8), int(pool.shape[0]), h, d,
+                                 _stream_ptr(stream)))
+
+
+def gqa_decode_workspace(batch: int, num_q_heads: int, num_kv_heads: int, max_context: int,
+                         window: int, head_dim: int):
+    torch = _torch()
+    n = int(lib.mqa_gqa_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, max_context,
+                                                window, head_dim))
+    return torch.empty(max(n, 256), dtype=torch.uint8, device="cuda") if n else None
+
+
+def gqa_decode_bf16(q, out, pool, num_kv_heads: int, block_table, context_lens, max_context: int,
+                    window: int, softmax_scale: float = 0.0, workspace=None, stream=None) -> None:
+    """``q`` bf16 [B, Hq, D]; ``out`` fp32 [B, Hq, D]; ``block_table`` int32
+    [B, max_pages]."""
+    torch = _torch()
+    b, hq, d = (int(x) for x in q.shape)
+    if tuple(out.shape) != (b, hq, d):
+        raise ValueError("out must have q's shape")
+    ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.mqa_gqa_decode_bf16(_dev_ptr(q, "q", torch.bfloat16),
+                                   _dev_ptr(out, "out", torch.float32),
+                                   _dev_ptr(pool, "pool", torch.uint8), int(pool.shape[0]),
+                                   num_kv_heads, d, _dev_ptr(block_table, "block_table", torch.int32),
+                                   int(block_table.shape[1]),
+                                   _dev_ptr(context_lens, "context_lens", torch.int32),
+                                   int(max_context), b, hq, int(window), float(softmax_scale),
+                                   ws_ptr, ws_bytes, _stream_ptr(stream)))
 
 
 _layout_cache = {}

@@ -233,3 +233,58 @@ def append(q: np.ndarray, context_lens: Sequence[int],
             out[li, t0:t1] = attend(rows, pos, win, ks_, kc, ksc, vc, vsc,
                                     scale).reshape(qlen, hq, d)
     return out
+
+
+# --------------------------------------------------------------------------
+# Grouped-query attention over a float (bf16) history: the baseline that
+# "Character.AI: inference optimization", section 03 (technique table),
+# compares multi-query attention with.  Written out in fp64 numpy from the
+# same definition as ``attend``: scores of the query against every key in its
+# range, softmax, weighted sum of the values.
+# --------------------------------------------------------------------------
+def attend_float(q: np.ndarray, pos: np.ndarray, window: np.ndarray, key_start: int,
+                 k: np.ndarray, v: np.ndarray, softmax_scale: float) -> np.ndarray:
+    """Attention of query rows ``q [R, d]`` over one float history ``k, v
+    [n, d]`` stored for positions ``key_start .. key_start + n - 1``; row r
+    attends ``[max(0, pos-W+1), pos]`` (``[0, pos]`` when W = 0).  fp64."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    r = q.shape[0]
+    out = np.empty_like(q)
+    for i in range(r):
+        p, w = int(pos[i]), int(window[i])
+        lo = max(0, p - w + 1) if w > 0 else 0
+        if lo < key_start or p - key_start >= k.shape[0]:
+            raise ValueError("query attends positions outside the stored history")
+        ks = k[lo - key_start:p - key_start + 1]
+        vs = v[lo - key_start:p - key_start + 1]
+        s = (ks @ q[i]) * softmax_scale
+        e = np.exp(s - s.max())
+        out[i] = (e @ vs) / e.sum()
+    return out
+
+
+def decode_gqa(q: np.ndarray, context_lens: Sequence[int], window: int, num_kv_heads: int,
+               kv: Callable[[int, int], Tuple[int, np.ndarray, np.ndarray]],
+               softmax_scale: Optional[float] = None) -> np.ndarray:
+    """One decode step of one grouped-query layer: ``q [B, Hq, d]``; query
+    head j reads KV head j // (Hq / num_kv_heads); ``kv(seq, head)`` gives
+    (key_start, k [n, d], v [n, d]).  Sequence b's query sits at position
+    context_lens[b] - 1.  Returns fp64 ``[B, Hq, d]`` (zeros for an empty
+    context)."""
+    q = np.asarray(q)
+    batch, hq, d = q.shape
+    group = hq // num_kv_heads
+    scale = default_scale(d) if softmax_scale is None else softmax_scale
+    out = np.zeros((batch, hq, d), dtype=np.float64)
+    for b in range(batch):
+        p = int(context_lens[b]) - 1
+        if p < 0:
+            continue
+        for h in range(num_kv_heads):
+            ks_, k, v = kv(b, h)
+            rows = q[b, h * group:(h + 1) * group]
+            out[b, h * group:(h + 1) * group] = attend_float(
+                rows, np.full(group, p), np.full(group, window), ks_, k, v, scale)
+    return out
