@@ -388,6 +388,9 @@ def main():
     roof["traffic"] = traffic_from_profile(w.case, kv_bytes)
     res["roofline"] = roof
     res["memory"] = memory_report(w, mk)
+    if w.kind == "decode" and not args.no_graph:
+        log("grouped-query bf16 baseline on the same step ...")
+        res["gqa8_bf16_baseline"] = gqa_report(w, mk, torch, ms_step)
     if w.kind == "append":
         log("prefix cache: offload and restore of the cached prefixes ...")
         res["memory"]["prefix_cache"] = prefix_restore_report(w, st, mk, torch)
@@ -439,6 +442,83 @@ def memory_report(w, mk, steps=200):
             "page_table_us_per_step": round(dt * 1e6, 1),
             "page_table_timing": f"one mqa_page_table_advance_all call (a decode step of the "
                                  f"{w.batch} sequences) from Python, mean of {steps} steps"}
+
+
+def gqa_report(w, mk, torch, mqa_ms, steps=200, kv_heads=8):
+    """The same decode step as grouped-query attention with 8 bf16 KV heads
+    (mqa_gqa_decode_bf16; "Character.AI: inference optimization", section
+    03: multi-query attention is 8X smaller than grouped-query attention).
+    One layer, the workload's batch, contexts, window and query heads; K/V
+    seeded N(0,1) in bf16, pages of the keys the step reads only, several
+    replicas so that the stream comes from HBM; HIP graph replay timed with
+    events, like the multi-query step."""
+    if w.num_layers != 1:
+        return None
+    dev = "cuda"
+    d, hq, b = w.head_dim, w.num_q_heads, w.batch
+    ctx = [int(c) for c in w.context_lens]
+    win = int(w.layer_window[0])
+    firsts = [max(0, c - win) // 16 if win > 0 else 0 for c in ctx]
+    pages = [(c - 1) // 16 + 1 - f for c, f in zip(ctx, firsts)]
+    max_pages = max((c - 1) // 16 + 1 for c in ctx)
+    num_pages = sum(pages)
+    pb = mk.gqa_page_bytes(kv_heads, d)
+    keys = sum(c - (max(0, c - win) if win > 0 else 0) for c in ctx)
+    kv_bytes = keys * kv_heads * 4 * d
+    reps = max(1, math.ceil(1.0e9 / (num_pages * pb)))
+    bt = np.zeros((b, max_pages), np.int32)
+    sm, at = [], 0
+    for i, (c, f, n) in enumerate(zip(ctx, firsts, pages)):
+        bt[i, f:f + n] = np.arange(at, at + n)
+        pos = np.arange(f * 16, c)
+        sm.append((bt[i, pos // 16].astype(np.int64) * 16 + pos % 16))
+        at += n
+    sm_t = torch.from_numpy(np.concatenate(sm)).to(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(5005)
+    pools = []
+    for r in range(reps):
+        pool = torch.zeros((num_pages, pb), dtype=torch.uint8, device=dev)
+        k = torch.randn((sm_t.numel(), kv_heads, d), generator=g, device=dev).to(torch.bfloat16)
+        v = torch.randn((sm_t.numel(), kv_heads, d), generator=g, device=dev).to(torch.bfloat16)
+        mk.gqa_pack_bf16(k, v, sm_t, pool, kv_heads)
+        pools.append(pool)
+    q = torch.randn((b, hq, d), generator=g, device=dev).to(torch.bfloat16)
+    outs = [torch.empty((b, hq, d), dtype=torch.float32, device=dev) for _ in range(reps)]
+    bt_t = torch.from_numpy(bt).to(dev)
+    cl = torch.tensor(ctx, dtype=torch.int32, device=dev)
+    ws = mk.gqa_decode_workspace(b, hq, kv_heads, w.max_context, win, d)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for r in range(reps):
+            mk.gqa_decode_bf16(q, outs[r], pools[r], kv_heads, bt_t, cl, w.max_context, win,
+                               workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        for r in range(reps):
+            mk.gqa_decode_bf16(q, outs[r], pools[r], kv_heads, bt_t, cl, w.max_context, win,
+                               workspace=ws)
+    gr.replay()
+    torch.cuda.synchronize()
+    n = max(1, steps // reps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        gr.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (n * reps)
+    gbs = kv_bytes / (ms * 1e-3) / 1e9
+    mqa_bytes = w.attended_keys() * (2 * d + 8)
+    return {"kv_heads": kv_heads, "dtype": "bf16", "kv_bytes_per_step": kv_bytes,
+            "us_per_step": round(ms * 1e3, 3), "gbs": round(gbs, 1),
+            "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "bytes_vs_mqa_int8": round(kv_bytes / mqa_bytes, 2),
+            "time_vs_mqa_int8_step": round(ms / mqa_ms, 2), "replicas": reps}
 
 
 def prefix_restore_report(w, st, mk, torch):
