@@ -258,7 +258,6 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
     return p;
   }
   a.num_groups = (int)keys.size();
-  for (int g = 0; g < 4 && g < a.num_groups; ++g) a.wg_begin4[g] = a.groups[g].wg_begin;
   a.total_wgs = (int)wg;
   a.total_merge = (int)merges;
   if (split) {

@@ -385,10 +385,7 @@ __device__ __forceinline__ void udiv_recip(uint32_t x, uint32_t d, uint32_t reci
 
 // The workgroup's (group, row block, chunk, sequence).  Kernel arguments are
 // read with scalar loads whose round trips add up when one address depends on
-// another, so every field the usual launches need sits at a fixed offset and
-// is read in one batch: the first four groups' first workgroups, group 0 and
-// its first row block.  Other workgroups read their group or row block at a
-// computed offset, one round trip later.
+// another; see decode_work for how the usual launch avoids that.
 // A kernel's first argument, read in place in the kernel-argument segment
 // (the first argument sits at offset 0).  Indexing a by-value argument with a
 // computed index makes the compiler copy the whole struct out of that segment
@@ -400,31 +397,48 @@ __device__ __forceinline__ const T* first_kernel_arg() {
 }
 
 __device__ __forceinline__ DecodeWork decode_work(const DecodeArgs& a, int w) {
-  const DecodeArgs* ka = first_kernel_arg<DecodeArgs>();
-  const int ng = a.num_groups;
-  const int wb1 = a.wg_begin4[1], wb2 = a.wg_begin4[2], wb3 = a.wg_begin4[3];
-  const DecodeGroup g0 = a.groups[0];
-  const RowBlock r0 = a.rbs[0];
-  int gi = (ng > 1 && w >= wb1) + (ng > 2 && w >= wb2) + (ng > 3 && w >= wb3);
   DecodeWork d;
-  if (gi == 0) {
-    d.g = g0;
-  } else {
-    if (gi == 3)
-      while (gi + 1 < ng && w >= ka->groups[gi + 1].wg_begin) ++gi;
-    d.g = ka->groups[gi];
-  }
   uint32_t q, r;
+  // The usual launch -- one (slot, window) group of at most four row blocks
+  // -- finds every field at a fixed offset, so it is worked out first, from
+  // one round of loads issued together; any other launch redoes it below.
+  const DecodeGroup g = a.groups[0];
+  const RowBlock r0 = a.rbs[0], r1 = a.rbs[1], r2 = a.rbs[2], r3 = a.rbs[3];
+  d.g = g;
+  udiv_recip((uint32_t)(w - g.wg_begin), (uint32_t)g.num_rb, g.rb_recip, q, r);
+  d.rbl = (int)r;
+  d.rb = r == 0 ? r0 : r == 1 ? r1 : r == 2 ? r2 : r3;
+  udiv_recip(q, (uint32_t)g.nchunk, g.ch_recip, q, r);
+  d.chunk = (int)r;
+  d.seq = (int)q;
+  if (a.num_groups == 1 && g.num_rb <= 4) return d;
+  // Any other launch: find the group, then read it and the row block at
+  // computed offsets (volatile: these reads stay apart from the ones above).
+  const volatile DecodeArgs* ka = first_kernel_arg<volatile DecodeArgs>();
+  const int ng = a.num_groups;
+  int gi = 0;
+  while (gi + 1 < ng && w >= ka->groups[gi + 1].wg_begin) ++gi;
+  const volatile DecodeGroup& vg = ka->groups[gi];
+  d.g.slot = vg.slot;
+  d.g.window = vg.window;
+  d.g.first_rb = vg.first_rb;
+  d.g.num_rb = vg.num_rb;
+  d.g.nchunk = vg.nchunk;
+  d.g.wg_begin = vg.wg_begin;
+  d.g.ws_begin = vg.ws_begin;
+  d.g.merge_begin = vg.merge_begin;
+  d.g.writes_new_kv = vg.writes_new_kv;
+  d.g.rb_recip = vg.rb_recip;
+  d.g.ch_recip = vg.ch_recip;
   udiv_recip((uint32_t)(w - d.g.wg_begin), (uint32_t)d.g.num_rb, d.g.rb_recip, q, r);
   d.rbl = (int)r;
   udiv_recip(q, (uint32_t)d.g.nchunk, d.g.ch_recip, q, r);
   d.chunk = (int)r;
   d.seq = (int)q;
-  const int rbi = d.g.first_rb + d.rbl;
-  if (rbi == 0)
-    d.rb = r0;
-  else
-    d.rb = ka->rbs[rbi];
+  const volatile RowBlock& vr = ka->rbs[d.g.first_rb + d.rbl];
+  d.rb.layer = vr.layer;
+  d.rb.head0 = vr.head0;
+  d.rb.nrows = vr.nrows;
   return d;
 }
 
@@ -722,6 +736,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(
   uint8_t* const stage = &ring.ring[wv][0][0];  // free until the first pages are issued
   sq.issue(stage, static_cast<const uint8_t*>(qp) + out_row0 * D * (QS == 1 ? 2 : 4), rb.nrows, wv,
            lane);
+  // the current token's rows do not depend on it either
+  CurrentToken<D, NK> cur;
+  if constexpr (NK != NewKV::kNone)
+    cur.load(k_new, v_new, (int64_t)g.slot * a.batch + seq, lane);
   const int ctx = clamp_ctx(context_lens[seq], a.max_context, a.max_pages);
   int lo, hi;
   decode_range(ctx, g.window, lo, hi);
@@ -756,9 +774,6 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(
     pid = __builtin_amdgcn_readlane(ids, min(max(pi - pbeg, 0), 63));
     return pi < pend && (uint32_t)pid < (uint64_t)a.num_pages;
   };
-  CurrentToken<D, NK> cur;
-  if constexpr (NK != NewKV::kNone)
-    cur.load(k_new, v_new, (int64_t)g.slot * a.batch + seq, lane);
   // q is converted before any page load is issued, so that waiting for it
   // does not wait for pages (the ids and the current token's rows, issued
   // after q, are needed right after it anyway).

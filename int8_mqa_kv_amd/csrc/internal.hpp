@@ -53,7 +53,6 @@ struct DecodeArgs {
   int32_t total_wgs;
   int32_t total_merge;  // row blocks x batch (one arrival counter each)
   float scale_log2;     // softmax scale * log2(e)
-  int32_t wg_begin4[4]; // groups[g].wg_begin of the first four groups (0 past the last)
   DecodeGroup groups[kMaxGroups];
   RowBlock rbs[kMaxRowBlocks];
 };
