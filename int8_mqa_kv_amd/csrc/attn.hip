@@ -347,11 +347,40 @@ __device__ __forceinline__ int clamp_ctx(int ctx, int max_context, int max_pages
   return min(max(ctx, 0), cap);
 }
 
-// Chunk count of a decode sequence: pages of [lo, hi) split ppc per chunk.
-__device__ __forceinline__ void decode_range(int ctx, int window, int& lo, int& hi) {
-  hi = ctx;
-  lo = window > 0 ? max(0, ctx - window) : 0;
-}
+// One wavefront's share of a decode sequence's key range [lo, hi): the
+// range's pages split over chunks of at least 16 pages (two per wavefront)
+// where the range allows, then evenly over the W wavefronts of the chunk.
+// A windowed range moves with the context length, so its chunks split the
+// range itself.  A global range always starts at key 0, so its chunk
+// boundaries are placed on the longest range the launch allows (ctx_cap
+// keys): they, and the pages every wavefront reads, then do not depend on
+// the sequence's own length, and a shorter sequence simply fills fewer
+// chunks (nch of them).  The critical path -- a chunk of the longest range --
+// is the same either way.
+template <int W>
+struct WaveSpan {
+  int lo, hi;      // keys
+  int p_last;      // last page of the range
+  int nch;         // chunks of the range that hold pages
+  int pbeg, pend;  // this wavefront's pages [pbeg, pend)
+
+  __device__ __forceinline__ WaveSpan(int ctx, int ctx_cap, int window, int nchunk, int chunk,
+                                      int wv) {
+    hi = ctx;
+    lo = window > 0 ? max(0, ctx - window) : 0;
+    const int p_first = lo >> 4;
+    p_last = (hi - 1) >> 4;
+    const int np = p_last - p_first + 1;
+    // (np <= 2^20 pages and chunks < 2^11 keep the products in 32 bits)
+    const int npb = window > 0 ? np : max((ctx_cap + kPageTokens - 1) / kPageTokens, 1);
+    const int nchb = min(nchunk, max(1, (npb + 2 * W - 1) / (2 * W)));
+    nch = window > 0 ? nchb : (int)(((uint32_t)(np * nchb) + npb - 1) / (uint32_t)npb);
+    const int cbeg = p_first + (int)((uint32_t)(chunk * npb) / (uint32_t)nchb);
+    const int npc = p_first + (int)((uint32_t)((chunk + 1) * npb) / (uint32_t)nchb) - cbeg;
+    pbeg = cbeg + wv * npc / W;
+    pend = max(pbeg, min(cbeg + (wv + 1) * npc / W, p_first + np));
+  }
+};
 
 // XCD-aware flat index: hardware workgroup x runs on XCD x % 8, so give each
 // XCD a contiguous range of logical work (gridDim.x is a multiple of 8).
@@ -740,9 +769,28 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(
   CurrentToken<D, NK> cur;
   if constexpr (NK != NewKV::kNone)
     cur.load(k_new, v_new, (int64_t)g.slot * a.batch + seq, lane);
-  const int ctx = clamp_ctx(context_lens[seq], a.max_context, a.max_pages);
-  int lo, hi;
-  decode_range(ctx, g.window, lo, hi);
+  // Nor, as a guess, do the page ids: they are loaded for the span of the
+  // longest context the launch allows (exact for a global range; for a
+  // windowed one whenever the sequence has that length) together with the
+  // length itself, and reloaded below only when the guess was wrong.
+  const int ctx_cap = clamp_ctx(a.max_context, a.max_context, a.max_pages);
+  const int32_t* table_row = block_table + ((int64_t)g.slot * a.batch + seq) * (int64_t)a.max_pages;
+  const WaveSpan<W> guess(ctx_cap, ctx_cap, g.window, g.nchunk, chunk, wv);
+  int ids = guess.pbeg + lane < guess.pend ? table_row[guess.pbeg + lane] : -1;
+  const int ctx_raw = context_lens[seq];
+  // All of the above are in flight together; wait for them here, before the
+  // branches below (the compiler would otherwise sink the loads whose values
+  // are used only past them, and each would cost a round trip of its own).
+  if constexpr (NK != NewKV::kNone) {
+#pragma unroll
+    for (int e = 0; e < CurrentToken<D, NK>::PER; ++e)
+      asm volatile("" ::"v"(cur.xk[e]), "v"(cur.xv[e]));
+  }
+  asm volatile("" ::"v"(ids), "v"(ctx_raw));
+  const int ctx = clamp_ctx(ctx_raw, a.max_context, a.max_pages);
+  WaveSpan<W> sp = guess;
+  if (ctx != ctx_cap) sp = WaveSpan<W>(ctx, ctx_cap, g.window, g.nchunk, chunk, wv);
+  const int lo = sp.lo, hi = sp.hi;
 
   if (hi <= lo) {  // empty context: zeros (and no current token to store)
     if (chunk == 0 && wv == 0) {
@@ -756,20 +804,11 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(
     }
     return;
   }
-  // This chunk's pages: the range's np pages split evenly over nch chunks of
-  // at least 16 pages (two per wavefront) where the range allows, then evenly
-  // over the W wavefronts.
-  const int p_first = lo >> 4, p_last = (hi - 1) >> 4;
-  const int np = p_last - p_first + 1;
-  const int nch = min(g.nchunk, max(1, (np + 2 * W - 1) / (2 * W)));
+  const int nch = sp.nch, p_last = sp.p_last;
   if (chunk >= nch) return;
-  // (np <= 2^20 pages and chunk < 2^11 keep the products in 32 bits)
-  const int cbeg = p_first + (int)((uint32_t)(chunk * np) / (uint32_t)nch);
-  const int npc = p_first + (int)((uint32_t)((chunk + 1) * np) / (uint32_t)nch) - cbeg;
-  const int pbeg = cbeg + wv * npc / W;
-  const int pend = cbeg + (wv + 1) * npc / W;
-  const int32_t* table_row = block_table + ((int64_t)g.slot * a.batch + seq) * (int64_t)a.max_pages;
-  const int ids = pbeg + lane < pend ? table_row[pbeg + lane] : -1;
+  const int pbeg = sp.pbeg, pend = sp.pend;
+  if (pbeg != guess.pbeg || pend > guess.pend)  // wave-uniform
+    ids = pbeg + lane < pend ? table_row[pbeg + lane] : -1;
   auto page_ok = [&](int pi, int& pid) {
     pid = __builtin_amdgcn_readlane(ids, min(max(pi - pbeg, 0), 63));
     return pi < pend && (uint32_t)pid < (uint64_t)a.num_pages;

@@ -165,3 +165,29 @@ def test_workspace_reuse_across_calls():
         again = g.decode(q)
         assert torch.equal(first, again)
     assert torch.equal(g._ws, ws1)
+
+
+@pytest.mark.parametrize("windows", [[0, 1024], [37, 0, 300]], ids=["global+1024", "mixed"])
+def test_loose_host_context_bound(windows):
+    """max_context far above every sequence's length, as a host may pass it
+    without reading the lengths back (the block table is widened to match, its
+    extra entries pointing at the poison page).  The page ids loaded for the
+    bound are then wrong for every windowed range and loaded again, and a
+    global range fills fewer chunks than the launch plans for."""
+    L = len(windows)
+    w = synth.custom_decode(12 + L, 5, 32, 128, "bf16", [1, 40, 1500, 5000, 9000], L, 0, 1500)
+    log(f"loose bound: windows {windows}, contexts {w.context_lens.tolist()}")
+    ls = [0] * L
+    g = GpuCase(w)
+    q, q64 = q_tensor(w)
+    extra = 2000                                  # pages beyond the longest range
+    bt = np.concatenate([w.block_table, np.full(w.block_table.shape[:2] + (extra,),
+                                                w.poison_page, np.int32)], axis=2)
+    bound = bt.shape[2] * 16
+    bt_t = torch.from_numpy(np.ascontiguousarray(bt)).cuda()
+    ws = mk.decode_workspace(w.batch, w.num_q_heads, ls, windows, bound, w.head_dim)
+    out = torch.full(tuple(q.shape), float("nan"), dtype=torch.float32, device="cuda")
+    mk.mqa_decode_attn(q, out, g.pool, bt_t, g.context_lens, bound, ls, windows, workspace=ws)
+    torch.cuda.synchronize()
+    want = oracle.decode(q64, w.context_lens, ls, windows, OracleKV(w))
+    assert_parity(out.cpu().numpy(), want, f"loose bound {windows}")
