@@ -806,12 +806,16 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(
   }
   const int nch = sp.nch, p_last = sp.p_last;
   if (chunk >= nch) return;
-  const int pbeg = sp.pbeg, pend = sp.pend;
+  // (wave-uniform: in scalar registers, so that the loop's page checks are
+  // scalar instructions)
+  const int pbeg = __builtin_amdgcn_readfirstlane(sp.pbeg);
+  const int pend = __builtin_amdgcn_readfirstlane(sp.pend);
+  const uint32_t pool_pages = (uint32_t)min<int64_t>(a.num_pages, 0xFFFFFFFF);
   if (pbeg != guess.pbeg || pend > guess.pend)  // wave-uniform
     ids = pbeg + lane < pend ? table_row[pbeg + lane] : -1;
   auto page_ok = [&](int pi, int& pid) {
     pid = __builtin_amdgcn_readlane(ids, min(max(pi - pbeg, 0), 63));
-    return pi < pend && (uint32_t)pid < (uint64_t)a.num_pages;
+    return pi < pend && (uint32_t)pid < pool_pages;
   };
   // q is converted before any page load is issued, so that waiting for it
   // does not wait for pages (the ids and the current token's rows, issued
@@ -1153,11 +1157,14 @@ __global__ __launch_bounds__(kAppendWaves * 64) void append_kernel(
   const int32_t* table_row = block_table + ((int64_t)slot * a.batch + seq) * (int64_t)a.max_pages;
   int wbase = pbeg;
   int ids = pbeg + lane < pend ? table_row[pbeg + lane] : -1;
-  // this wavefront's share of block `blk`'s loads into ring slot `rs`
+  // this wavefront's share of block `blk`'s loads into ring slot `rs` (the
+  // wavefront index read as uniform, so that the page checks are scalar)
+  const int wvs = __builtin_amdgcn_readfirstlane(wv);
+  const uint32_t pool_pages = (uint32_t)min<int64_t>(a.num_pages, 0xFFFFFFFF);
   auto issue_block = [&](int blk, int rs) {
 #pragma unroll
     for (int i = 0; i < MY_PIECES_MAX; ++i) {
-      const int k = wv + i * W;
+      const int k = wvs + i * W;
       if (k >= PIECES) break;  // wave-uniform
       const int u = k < 2 * KIB ? k / KIB : k - 2 * KIB;
       const int pg = pbeg + 2 * blk + u;
@@ -1166,7 +1173,7 @@ __global__ __launch_bounds__(kAppendWaves * 64) void append_kernel(
         ids = pg + lane < pend ? table_row[pg + lane] : -1;
       }
       const int pid = __builtin_amdgcn_readlane(ids, min(max(pg - wbase, 0), 63));
-      const bool ok = pg < pend && (uint32_t)pid < (uint64_t)a.num_pages;
+      const bool ok = pg < pend && (uint32_t)pid < pool_pages;
       const uint8_t* rec = pool + (int64_t)(ok ? pid : 0) * page_bytes(D);
       uint8_t* dst = sm.ring[rs][u];
       if (k < 2 * KIB) {
@@ -1180,7 +1187,7 @@ __global__ __launch_bounds__(kAppendWaves * 64) void append_kernel(
   };
   // loads per block issued by this wavefront (constant: every block issues
   // all its pieces; blocks past the range load page 0, unused)
-  const int mine = (PIECES - wv + W - 1) / W;
+  const int mine = (PIECES - wvs + W - 1) / W;
 #pragma unroll
   for (int i = 0; i < RB - 1; ++i) issue_block(i, i);
 
