@@ -191,3 +191,13 @@ def test_loose_host_context_bound(windows):
     torch.cuda.synchronize()
     want = oracle.decode(q64, w.context_lens, ls, windows, OracleKV(w))
     assert_parity(out.cpu().numpy(), want, f"loose bound {windows}")
+
+
+@pytest.mark.parametrize("window", [0, 300], ids=["global", "window300"])
+def test_many_ragged_sequences(window):
+    """130 sequences of ragged lengths (1 to 1500 tokens): the kernel reads the
+    lengths 64 at a time and shares its workgroups out over the sequences in
+    chunks sized from the true page counts."""
+    ctx = [1 + (37 * i * i + 11 * i) % 1500 for i in range(130)]
+    w = synth.custom_decode(20 + (window > 0), 130, 32, 128, "bf16", ctx, 1, window, 0)
+    _run_case(w)
