@@ -174,7 +174,11 @@ size_t mqa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
  *                the attended keys, khat = sK*codeK, vhat = sV*codeV.
  *  block_table   int32 [num_slots][batch][max_pages_per_seq]: page ids in
  *                the pool of the logical pages 0,1,2,... of each sequence in
- *                each slot.  Entries for pages not attended are not read.
+ *                each slot.  Entries up to page ceil(max_context/16)-1 of a
+ *                row may be read even where the sequence does not attend them
+ *                (the page ids are fetched for the bound's range before the
+ *                length is known), but no page is ever loaded through such an
+ *                entry: they may hold any value.
  *  context_lens  int32 [batch]: cached tokens of each sequence including the
  *                current one (which sits at position context_len-1).  Must
  *                lie in [1, max_context]; a length <= 0 gives zeros.
