@@ -261,42 +261,34 @@ __device__ __forceinline__ void attend_block(WaveState<D, NRT>& st, const QOps<D
   st.ev = ev_new;
   const float pvm = ev_new == kNoExp ? 0.0f : ldexp2(1.0f, kPvBias - ev_new);
 
-  f16x8 pop[NRT];
-  float alpha[NRT];
+  // Row maxima and the lazy reference first: whether the accumulators need
+  // rescaling is known before any exponent, so the rescale branch comes
+  // before the exponents and the PV products, which then share one block of
+  // code (the P of one row tile is computed while the other tile's PV
+  // products run on the matrix cores).
+  float t[NRT][2][4];
+  float alpha[NRT], neg_m[NRT];
   bool rescale = false;
 #pragma unroll
   for (int n = 0; n < NRT; ++n) {
     // t = int score * key scale; the row's factor crow (> 0) is applied in
     // the exponent's FMA, so the row max is taken on t
-    float t[2][4];
     float mt = kNegInf;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float x = s[n][u][r] * (u ? p1.sk : p0.sk)[r];
-        t[u][r] = MASKED ? (valid[u][r] ? x : kNegInf) : x;
-        mt = fmaxf(mt, t[u][r]);
+        t[n][u][r] = MASKED ? (valid[u][r] ? x : kNegInf) : x;
+        mt = fmaxf(mt, t[n][u][r]);
       }
     mt = row_max4(mt);
-    const float c = q.crow[n];
-    const float mx = mt == kNegInf ? kNegInf : mt * c;
+    const float mx = mt == kNegInf ? kNegInf : mt * q.crow[n];
     const bool move = mx > st.m[n] + kTau;  // also true for the first valid block
     const float m_new = move ? mx : st.m[n];
     alpha[n] = move ? fast_exp2(st.m[n] - m_new) : 1.0f;  // exp2(-inf) = 0
     rescale |= move;
-    const float neg_m = m_new == kNegInf ? 0.0f : -m_new;
-    float ps = 0.0f;
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float pr = fast_exp2(__builtin_fmaf(t[u][r], c, neg_m));
-        ps += pr;
-        const float pv = pr * ((u ? p1.sv : p0.sv)[r] * pvm);
-        pop[n][4 * u + r] = (_Float16)(MASKED ? (valid[u][r] ? pv : 0.0f) : pv);
-      }
-    st.l[n] = st.l[n] * alpha[n] + ps;
+    neg_m[n] = m_new == kNegInf ? 0.0f : -m_new;
     st.m[n] = m_new;
   }
   // rescale the accumulators only when some row's reference moved or the V
@@ -311,6 +303,21 @@ __device__ __forceinline__ void attend_block(WaveState<D, NRT>& st, const QOps<D
     }
   }
 
+  f16x8 pop[NRT];
+#pragma unroll
+  for (int n = 0; n < NRT; ++n) {
+    float ps = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float pr = fast_exp2(__builtin_fmaf(t[n][u][r], q.crow[n], neg_m[n]));
+        ps += pr;
+        const float pv = pr * ((u ? p1.sv : p0.sv)[r] * pvm);
+        pop[n][4 * u + r] = (_Float16)(MASKED ? (valid[u][r] ? pv : 0.0f) : pv);
+      }
+    st.l[n] = st.l[n] * alpha[n] + ps;
+  }
   // V codes enter as c + kVBias (two byte permutes per four codes); the
   // matching sum of P comes from one more product with an all-ones operand,
   // so it uses the very fp16 P values the accumulators saw.
