@@ -5,7 +5,7 @@ import torch
 
 import oracle
 import synth
-from tests.gpu_util import GpuCase, OracleKV, assert_parity, log, q_tensor
+from tests.gpu_util import GpuCase, OracleKV, assert_parity, assert_parity_peaked, log, q_tensor
 
 pytestmark = pytest.mark.gpu
 
@@ -67,3 +67,15 @@ def test_case4_hybrid_turn_sampled():
     order = np.argsort(w.context_lens)
     seqs = sorted(set([int(order[0]), int(order[-1]), int(order[len(order) // 2]), 7, 101, 200]))
     _run(w, seqs=seqs)
+
+
+def test_append_peaked_softmax():
+    """q scaled by 16 (exact in bf16): concentrated weights over a causal chunk."""
+    w = synth.custom_append(47, [900, 3000], [64, 17], 32, 128, [1024, 0], [0, 1])
+    g = GpuCase(w)
+    q, q64 = q_tensor(w)
+    q, q64 = q * 16, q64 * 16
+    out = g.append(q)
+    want = oracle.append(q64, w.context_lens, w.cu_q_lens, w.layer_slot, w.layer_window,
+                         OracleKV(w))
+    assert_parity_peaked(out.cpu().numpy(), want, w, "append, peaked softmax")

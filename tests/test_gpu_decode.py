@@ -10,7 +10,7 @@ import torch
 import int8_mqa_kv_amd as mk
 import oracle
 import synth
-from tests.gpu_util import GpuCase, OracleKV, assert_parity, log, q_tensor
+from tests.gpu_util import GpuCase, OracleKV, assert_parity, assert_parity_peaked, log, q_tensor
 
 pytestmark = pytest.mark.gpu
 
@@ -201,3 +201,18 @@ def test_many_ragged_sequences(window):
     ctx = [1 + (37 * i * i + 11 * i) % 1500 for i in range(130)]
     w = synth.custom_decode(20 + (window > 0), 130, 32, 128, "bf16", ctx, 1, window, 0)
     _run_case(w)
+
+
+@pytest.mark.parametrize("window", [0, 1024], ids=["global", "window1024"])
+def test_peaked_softmax(window):
+    """q scaled by 16 (exact in bf16): every row's weights concentrate on a
+    few keys, where the fp16 P operand's rounding shows most, and the running
+    maximum moves in large steps."""
+    w = synth.custom_decode(30 + (window > 0), 4, 32, 128, "bf16", [300, 1500, 4096, 9000], 1,
+                            window, 2000)
+    g = GpuCase(w)
+    q, q64 = q_tensor(w)
+    q, q64 = q * 16, q64 * 16
+    out = g.decode(q)
+    want = oracle.decode(q64, w.context_lens, w.layer_slot, w.layer_window, OracleKV(w))
+    assert_parity_peaked(out.cpu().numpy(), want, w, f"peaked softmax, window {window}")
