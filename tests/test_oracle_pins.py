@@ -161,6 +161,25 @@ def test_two_keys_logistic_weights():
     assert out0[0, 0] == 127.0
 
 
+def test_huge_scores_select_the_argmax_key():
+    """Scores of order 1e4: the softmax is one-hot on the largest score.  The
+    oracle must take the maximum out before exponentiating (exp of such
+    scores overflows fp64, giving inf/inf) and return that key's value."""
+    d, n = 64, 40
+    kc, ks = oracle.quantize(_rows(12, n, d))
+    vc, vs = oracle.quantize(_rows(13, n, d))
+    q = _rows(14, 3, d) * np.float32(2000)
+    out = oracle.attend(q, np.full(3, n - 1), np.zeros(3), 0, kc, ks, vc, vs, 1 / math.sqrt(d))
+    assert np.all(np.isfinite(out))
+    scores = q.astype(np.float64) @ oracle.dequantize(kc, ks).T / math.sqrt(d)
+    assert scores.max() > 1000
+    vh = oracle.dequantize(vc, vs)
+    for r in range(3):
+        top2 = np.sort(scores[r])[-2:]
+        assert top2[1] - top2[0] > 40  # the runner-up weighs less than e^-40
+        np.testing.assert_allclose(out[r], vh[int(np.argmax(scores[r]))], rtol=0, atol=1e-15)
+
+
 def test_constant_values_pass_through():
     d, n = 128, 300
     kc, ks, _, _ = _single_history(n, d, 10)
