@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MQA_KV_ABI_VERSION 3
+#define MQA_KV_ABI_VERSION 4
 #define MQA_PAGE_TOKENS 16
 
 typedef enum {
@@ -78,7 +78,9 @@ typedef enum {
  * in one record so that one page read brings everything attention needs.
  * Byte positions inside a record are given by mqa_page_offset(); the order is
  * chosen so that each GPU lane's matrix-core operand is one contiguous
- * 16-byte load.  Pages of every slot come from the same pool; which page
+ * 16-byte load.  A K code c (-127..127) is stored as the int8 byte c; a V
+ * code c is stored as the unsigned byte c + 128 (c with its sign bit
+ * flipped), the form the fp16 operand conversion takes as it is.  Pages of every slot come from the same pool; which page
  * holds which tokens is decided by the caller's block tables.
  */
 typedef struct mqa_kv_pool {

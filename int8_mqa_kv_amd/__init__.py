@@ -620,14 +620,15 @@ def unpack_page_tokens(pool_bytes: np.ndarray, slots: np.ndarray, head_dim: int)
 
     ``pool_bytes`` uint8 [num_pages, page_bytes]; ``slots`` int64 [T]
     (page*16 + offset).  Returns ``(k_codes int8 [T, D], k_scales f32 [T],
-    v_codes int8 [T, D], v_scales f32 [T])``."""
+    v_codes int8 [T, D], v_scales f32 [T])``.  A V code c is stored as the
+    byte c + 128 (its sign bit flipped); K codes as plain int8."""
     k_off, v_off, ks_off, vs_off = page_layout(head_dim)
     slots = np.asarray(slots, dtype=np.int64)
     page, j = slots // PAGE_TOKENS, slots % PAGE_TOKENS
     rec = pool_bytes[page]                                   # [T, page_bytes]
     rows = np.arange(slots.size)[:, None]
     kc = rec[rows, k_off[j]].view(np.int8)
-    vc = rec[rows, v_off[j]].view(np.int8)
+    vc = (rec[rows, v_off[j]] ^ np.uint8(0x80)).view(np.int8)
     ks = np.stack([rec[np.arange(slots.size), ks_off[j] + b] for b in range(4)], 1).copy()
     vs = np.stack([rec[np.arange(slots.size), vs_off[j] + b] for b in range(4)], 1).copy()
     return kc, ks.view(np.float32).reshape(-1), vc, vs.view(np.float32).reshape(-1)

@@ -325,8 +325,8 @@ __device__ __forceinline__ void attend_block(WaveState<D, NRT>& st, const QOps<D
   for (int t = 0; t < Geo<D>::VT; ++t) {
     const int h = t >> 2, dw = t & 3;
     f16x2 a0, a1, b0, b1;
-    i8x4_to_f16x4_biased(p0.v[h][dw], a0, a1);
-    i8x4_to_f16x4_biased(p1.v[h][dw], b0, b1);
+    v_bytes_to_f16x4_biased(p0.v[h][dw], a0, a1);
+    v_bytes_to_f16x4_biased(p1.v[h][dw], b0, b1);
     const f16x8 vop = {a0[0], a0[1], a1[0], a1[1], b0[0], b0[1], b1[0], b1[1]};
 #pragma unroll
     for (int n = 0; n < NRT; ++n) st.acc[n][t] = mma16(vop, pop[n], st.acc[n][t]);
@@ -712,7 +712,7 @@ struct CurrentToken {
     for (int e = 0; e < PER; ++e) {
       const int c = lane * PER + e;
       rec[k_code_offset(D, j, c)] = (uint8_t)ck[e];
-      rec[v_code_offset(D, j, c)] = (uint8_t)cv[e];
+      rec[v_code_offset(D, j, c)] = v_code_byte(cv[e]);
     }
     if (lane == 0) {
       *reinterpret_cast<float*>(rec + k_scale_offset(D, j)) = sk;

@@ -26,38 +26,18 @@ __device__ __forceinline__ T bitcast(F f) {
   return __builtin_bit_cast(T, f);
 }
 
-// Four int8 codes (one dword, byte k = code k) -> four exact fp16 values.
-// Bias each byte to u = code + 128 (xor 0x80), place it under the fp16
-// exponent of 1024 (bits 0x64uu = 1024 + u, exact for u < 1024) with one byte
-// permute per pair, then subtract 1152 = 1024 + 128 with a packed fp16 add.
-// Every step is exact: the results are the integers -127..127.
-__device__ __forceinline__ void i8x4_to_f16x4(uint32_t w, f16x2& lo, f16x2& hi) {
-  const uint32_t u = w ^ 0x80808080u;
+// Four stored V bytes (one dword, byte k = code k + 128) -> four exact fp16
+// values c + kVBias.  Each byte goes under the fp16 exponent of 1024 (bits
+// 0x64uu = 1024 + u, exact for u < 1024) with one byte permute per pair, so
+// the value is 1024 + 128 + c = 1152 + c.  A product of these with P carries
+// kVBias * sum(P), which the caller removes once, from the same P summed on
+// the matrix cores.
+constexpr float kVBias = 1152.0f;
+__device__ __forceinline__ void v_bytes_to_f16x4_biased(uint32_t u, f16x2& lo, f16x2& hi) {
   // v_perm_b32: selector bytes 0-3 pick bytes of the second operand, 4-7 of
   // the first.  Result bytes (low to high): u.b0, 0x64, u.b1, 0x64.
-  const uint32_t a = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
-  const uint32_t b = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
-  const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-  lo = bitcast<f16x2>(a) - bias;
-  hi = bitcast<f16x2>(b) - bias;
-}
-
-// The same four codes as fp16 values c + kVBias (1152 + c, exact), without the
-// subtraction: a product of these with P carries kVBias * sum(P), which the
-// caller removes once, from the same P summed on the matrix cores.
-constexpr float kVBias = 1152.0f;
-__device__ __forceinline__ void i8x4_to_f16x4_biased(uint32_t w, f16x2& lo, f16x2& hi) {
-  const uint32_t u = w ^ 0x80808080u;
   lo = bitcast<f16x2>(__builtin_amdgcn_perm(0x64646464u, u, 0x04010400u));
   hi = bitcast<f16x2>(__builtin_amdgcn_perm(0x64646464u, u, 0x04030402u));
-}
-
-// Eight codes in two dwords -> one f16x8 operand (element k = byte k).
-__device__ __forceinline__ f16x8 i8x8_to_f16x8(uint32_t w0, uint32_t w1) {
-  f16x2 a, b, c, d;
-  i8x4_to_f16x4(w0, a, b);
-  i8x4_to_f16x4(w1, c, d);
-  return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 // D = A.B + C on one 16x16x32 fp16 tile, fp32 accumulate.  Lane l

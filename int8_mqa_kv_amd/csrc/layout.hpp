@@ -21,6 +21,11 @@
 // The result is that every operand load is perfectly coalesced (a wavefront
 // reads 1 KiB of consecutive bytes per instruction) and needs no LDS
 // transpose.
+//
+// K codes are stored as two's-complement int8.  V codes are stored with the
+// sign bit flipped (byte = code xor 0x80 = code + 128, an unsigned byte): the
+// fp16 operand conversion places that byte under a fixed exponent as it is,
+// with no per-dword fix-up in the attention loop.
 #pragma once
 #include <stdint.h>
 
@@ -49,6 +54,9 @@ MQA_HD constexpr int v_code_offset(int D, int j, int c) {
   return 16 * D + ((c >> 4) >> 2) * 1024 + (j >> 2) * 256 + (c & 15) * 16 +
          ((c >> 4) & 3) * 4 + (j & 3);
 }
+
+// Stored byte of V code c (-127..127): c + 128.
+MQA_HD constexpr uint8_t v_code_byte(int c) { return (uint8_t)(c ^ 0x80); }
 
 MQA_HD constexpr int k_scale_offset(int D, int j) { return 32 * D + 4 * j; }
 MQA_HD constexpr int v_scale_offset(int D, int j) { return 32 * D + 64 + 4 * j; }

@@ -50,7 +50,8 @@ __global__ __launch_bounds__(kPackWaves * 64) void pack_kernel(
     for (int e = 0; e < PER; ++e) {
       const int c = lane * PER + e;
       const int off = which == 0 ? k_code_offset(D, j, c) : v_code_offset(D, j, c);
-      rec[off] = (uint8_t)(int8_t)quant_code(x[e], a, s);
+      const int code = quant_code(x[e], a, s);
+      rec[off] = which == 0 ? (uint8_t)(int8_t)code : v_code_byte(code);
     }
     if (lane == 0) {
       const int off = which == 0 ? k_scale_offset(D, j) : v_scale_offset(D, j);

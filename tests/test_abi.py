@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_sizes():
-    assert mk.lib.mqa_abi_version() == 3
+    assert mk.lib.mqa_abi_version() == 4
     assert mk.page_bytes(128) == 32 * 128 + 128 == 4224
     assert mk.page_bytes(64) == 2176
     assert mk.lib.mqa_page_bytes(96) == 0
@@ -143,7 +143,7 @@ def test_unpack_roundtrip_on_host():
     vs = g.random(16).astype(np.float32)
     page = np.zeros(mk.page_bytes(d), np.uint8)
     page[k_off] = kc.view(np.uint8)
-    page[v_off] = vc.view(np.uint8)
+    page[v_off] = (vc.astype(np.int16) + 128).astype(np.uint8)  # V codes stored as c + 128
     for j in range(16):
         page[ks_off[j]:ks_off[j] + 4] = np.frombuffer(ks[j].tobytes(), np.uint8)
         page[vs_off[j]:vs_off[j] + 4] = np.frombuffer(vs[j].tobytes(), np.uint8)
