@@ -148,9 +148,11 @@ int kv_pack_int8(const void* k, const void* v, mqa_dtype src_dtype,
  * arguments (the host arrays are read).  Contexts long enough to be split
  * across workgroups leave softmax partials (max, sum, weighted values) there;
  * the last of them to arrive merges them inside the same kernel.  The first
- * 8 MiB of a workspace hold the arrival counters (8 per 32-head row block of
- * a layer and sequence, each on its own 128-byte line; at most 8192 such
- * pairs per call), the partials follow.
+ * 8 MiB of a workspace hold the arrival counters (one per wavefront of a
+ * workgroup, 8 or 4, per 32-head row block of a layer and sequence, each on
+ * its own 128-byte line; at most 8192 such pairs per call), the partials
+ * follow.  The size depends on the decode tuning in force
+ * (mqa_decode_tuning); query it again after changing that.
  * Returns 0 when none is needed or the arguments are invalid (a following
  * call reports why).  The workspace must be zero-filled ONCE before its first
  * use (e.g. hipMemset after allocation); every call leaves the counters at
@@ -160,6 +162,24 @@ size_t mqa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                   int32_t num_layers, const int32_t* layer_slot,
                                   const int32_t* layer_window,
                                   int32_t max_context, int32_t head_dim);
+
+/*
+ * Decode tuning (not part of what is computed: results depend on it only
+ * through the rounding order of the merges).  Process-wide; not thread-safe
+ * against concurrent decode calls or workspace queries.  Each argument is 0
+ * for "the planner decides" or a forced value:
+ *  waves       wavefronts per decode workgroup: 8 (one workgroup per CU) or
+ *              4 (two per CU).  The planner takes 4 only when the 8-wavefront
+ *              plan leaves more than 15 % of the CUs idle and 4 fills at
+ *              least 10 % more of the slots with at most 8 chunks per item.
+ *  rows        query rows per row block: 8, 16 or 32.
+ *  target_wgs  workgroups of 8 wavefronts the planner aims for (default 256,
+ *              one per CU of an MI355X).
+ * Starts from the environment variables MQA_DECODE_WAVES, MQA_DECODE_ROWS and
+ * MQA_DECODE_TARGET_WGS.  Returns MQA_OK, or MQA_ERR_INVALID (nothing
+ * changed) for a value outside those sets or a negative target.
+ */
+int mqa_decode_tuning(int32_t waves, int32_t rows, int32_t target_wgs);
 
 /*
  * mqa_decode_attn -- one decode step of multi-query attention over the paged

@@ -75,6 +75,8 @@ def _load() -> ctypes.CDLL:
     L.kv_pack_int8.restype = ctypes.c_int
     L.mqa_decode_workspace_bytes.argtypes = [i32, i32, i32, p, p, i32, i32]
     L.mqa_decode_workspace_bytes.restype = sz
+    L.mqa_decode_tuning.argtypes = [i32, i32, i32]
+    L.mqa_decode_tuning.restype = ctypes.c_int
     L.mqa_decode_attn.argtypes = [p, ctypes.c_int, p, ctypes.POINTER(_Pool), p, i32, p, i32, i32,
                                   i32, i32, i32, p, p, f32, p, sz, p]
     L.mqa_decode_attn.restype = ctypes.c_int
@@ -501,6 +503,12 @@ def decode_workspace_bytes(batch: int, num_q_heads: int, layer_slot: Sequence[in
     lw = _host_i32(layer_window, n, "layer_window")
     return int(lib.mqa_decode_workspace_bytes(batch, num_q_heads, n, ls.ctypes.data,
                                               lw.ctypes.data, max_context, head_dim))
+
+
+def decode_tuning(waves: int = 0, rows: int = 0, target_wgs: int = 0) -> None:
+    """Process-wide decode tuning (``mqa_decode_tuning``); 0 = the planner
+    decides.  Workspace sizes depend on it: query them after a change."""
+    _check(lib.mqa_decode_tuning(int(waves), int(rows), int(target_wgs)))
 
 
 def decode_workspace(batch: int, num_q_heads: int, layer_slot: Sequence[int],

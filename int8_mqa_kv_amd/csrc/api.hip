@@ -112,32 +112,38 @@ float scale_log2_of(float softmax_scale, int head_dim) {
 struct DecodePlan {
   DecodeArgs args;
   int nrt = 2;
+  int waves = kDecodeWaves;   // wavefronts per workgroup
   size_t ws_bytes = 0;        // partial records + arrival counters
   int rc = MQA_OK;
 };
 
-// Workgroups the planner aims for: one per compute unit of the 256, each with
-// kDecodeWaves wavefronts keeping pages in flight.  MQA_DECODE_TARGET_WGS
-// overrides it (a tuning aid; results do not depend on it beyond rounding).
-int target_workgroups() {
-  static const int v = [] {
-    const char* e = getenv("MQA_DECODE_TARGET_WGS");
-    const int t = e ? atoi(e) : 0;
-    return t > 0 ? t : 256;
+// Decode tuning overrides (0 = the planner decides), process-wide.  They start
+// from MQA_DECODE_WAVES (4 or 8), MQA_DECODE_ROWS (8, 16 or 32) and
+// MQA_DECODE_TARGET_WGS, and mqa_decode_tuning() replaces them.  Results do
+// not depend on them beyond rounding order.
+struct DecodeTuning {
+  int waves = 0, rows = 0, target_wgs = 0;
+};
+DecodeTuning& tuning() {
+  static DecodeTuning t = [] {
+    DecodeTuning d;
+    auto env = [](const char* name) {
+      const char* e = getenv(name);
+      return e ? atoi(e) : 0;
+    };
+    const int w = env("MQA_DECODE_WAVES"), r = env("MQA_DECODE_ROWS"), g = env("MQA_DECODE_TARGET_WGS");
+    d.waves = (w == kDecodeWaves || w == kDecodeWavesSmall) ? w : 0;
+    d.rows = (r == 8 || r == 16 || r == 32) ? r : 0;
+    d.target_wgs = g > 0 ? g : 0;
+    return d;
   }();
-  return v;
+  return t;
 }
 
-// MQA_DECODE_ROWS = 8, 16 or 32 forces the query rows per row block (a
-// tuning aid, like MQA_DECODE_TARGET_WGS); 0 when unset.
-int decode_rows_override() {
-  static const int v = [] {
-    const char* e = getenv("MQA_DECODE_ROWS");
-    const int t = e ? atoi(e) : 0;
-    return (t == 8 || t == 16 || t == 32) ? t : 0;
-  }();
-  return v;
-}
+// Workgroups of kDecodeWaves wavefronts the planner aims for: one per compute
+// unit of the 256 (twice as many of the four-wavefront shape).
+int target_workgroups() { return tuning().target_wgs > 0 ? tuning().target_wgs : 256; }
+int decode_rows_override() { return tuning().rows; }
 
 // Query rows per row block.  32 rows (two 16-row tiles per wavefront) read
 // each page once for the most rows and cost the least vector work per (row,
@@ -158,8 +164,9 @@ int decode_rows(int num_q_heads, int num_layers, int64_t max_span_pages, int64_t
 
 DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
                        const int32_t* layer_slot, const int32_t* layer_window,
-                       int32_t max_context, int32_t head_dim) {
+                       int32_t max_context, int32_t head_dim, int waves) {
   DecodePlan p;
+  p.waves = waves;
   DecodeArgs& a = p.args;
   memset(&a, 0, sizeof a);
   // groups of layers reading one slot with one window, in first-seen order
@@ -214,11 +221,11 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
   // the item's span, so that one round of workgroups covers the launch with
   // equal work per workgroup and none left idle; at least enough chunks that
   // no wavefront takes more than 64 pages (one register of page ids).
-  const int64_t target = std::max<int64_t>(target_workgroups(), items);
+  const int64_t target = std::max<int64_t>(target_workgroups() * (kDecodeWaves / waves), items);
   std::vector<int64_t> nchunk(keys.size());
   for (size_t g = 0; g < keys.size(); ++g) {
     const int64_t share = target * max_np[g] / std::max<int64_t>(work, 1);
-    const int64_t need = (max_np[g] + 64 * kDecodeWaves - 1) / (64 * kDecodeWaves);
+    const int64_t need = (max_np[g] + 64 * waves - 1) / (64 * waves);
     nchunk[g] = std::max<int64_t>({1, share, need});
   }
 
@@ -262,15 +269,44 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
   a.total_merge = (int)merges;
   if (split) {
     // the fixed counter prefix, then the partial records
-    if (merges * kDecodeWaves > kDecodeCounters) {
+    if (merges * waves > kDecodeCounters) {
       p.rc = fail(MQA_ERR_UNSUPPORTED,
                   "%lld (row block, sequence) pairs with split contexts in one call; at most %lld",
-                  (long long)merges, (long long)(kDecodeCounters / kDecodeWaves));
+                  (long long)merges, (long long)(kDecodeCounters / waves));
       return p;
     }
     p.ws_bytes = (size_t)(kCounterWords + ws * ws_record_floats(head_dim)) * sizeof(float);
   }
   return p;
+}
+
+// The workgroup shape of a launch.  Eight wavefronts per workgroup, one
+// workgroup per CU, unless that plan leaves more than 15 % of the CUs idle
+// (few items, each split into whole chunks) and four-wavefront workgroups, two
+// per CU, fill at least 10 % more of the slots with at most 8 chunks per item
+// (the last arrival folds every chunk's record).
+DecodePlan plan_decode_auto(int32_t batch, int32_t num_q_heads, int32_t num_layers,
+                            const int32_t* layer_slot, const int32_t* layer_window,
+                            int32_t max_context, int32_t head_dim) {
+  if (tuning().waves)
+    return plan_decode(batch, num_q_heads, num_layers, layer_slot, layer_window, max_context,
+                       head_dim, tuning().waves);
+  DecodePlan p8 = plan_decode(batch, num_q_heads, num_layers, layer_slot, layer_window,
+                              max_context, head_dim, kDecodeWaves);
+  if (p8.rc) return p8;
+  const double slots = target_workgroups();
+  const double fill8 = p8.args.total_wgs / slots;
+  if (fill8 >= 0.85) return p8;
+  DecodePlan p4 = plan_decode(batch, num_q_heads, num_layers, layer_slot, layer_window,
+                              max_context, head_dim, kDecodeWavesSmall);
+  if (p4.rc) {
+    ok();  // the eight-wavefront plan stands; clear the other's message
+    return p8;
+  }
+  int max_chunks = 0;
+  for (int g = 0; g < p4.args.num_groups; ++g) max_chunks = std::max(max_chunks, p4.args.groups[g].nchunk);
+  const double fill4 = p4.args.total_wgs / (slots * (kDecodeWaves / kDecodeWavesSmall));
+  return (max_chunks <= 8 && fill4 <= 1.0 && fill4 >= fill8 + 0.10) ? p4 : p8;
 }
 
 }  // namespace
@@ -342,9 +378,22 @@ size_t mqa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
     return 0;
   for (int l = 0; l < num_layers; ++l)
     if (layer_slot[l] < 0 || layer_window[l] < 0) return 0;
-  DecodePlan p = plan_decode(batch, num_q_heads, num_layers, layer_slot, layer_window,
-                             max_context, head_dim);
+  DecodePlan p = plan_decode_auto(batch, num_q_heads, num_layers, layer_slot, layer_window,
+                                  max_context, head_dim);
   return p.rc ? 0 : p.ws_bytes;
+}
+
+int mqa_decode_tuning(int32_t waves, int32_t rows, int32_t target_wgs) {
+  if (waves != 0 && waves != kDecodeWaves && waves != kDecodeWavesSmall)
+    return fail(MQA_ERR_INVALID, "waves %d: 0, %d or %d", waves, kDecodeWavesSmall, kDecodeWaves);
+  if (rows != 0 && rows != 8 && rows != 16 && rows != 32)
+    return fail(MQA_ERR_INVALID, "rows %d: 0, 8, 16 or 32", rows);
+  if (target_wgs < 0) return fail(MQA_ERR_INVALID, "target_wgs %d < 0", target_wgs);
+  DecodeTuning& t = tuning();
+  t.waves = waves;
+  t.rows = rows;
+  t.target_wgs = target_wgs;
+  return ok();
 }
 
 }  // extern "C"
@@ -363,8 +412,8 @@ int decode_common(const void* q, mqa_dtype q_dtype, float* out, const void* k_ne
                              max_context, batch, num_q_heads, num_layers, num_slots, layer_slot,
                              layer_window);
   if (rc) return rc;
-  DecodePlan p = plan_decode(batch, num_q_heads, num_layers, layer_slot, layer_window, max_context,
-                             pool->head_dim);
+  DecodePlan p = plan_decode_auto(batch, num_q_heads, num_layers, layer_slot, layer_window,
+                                  max_context, pool->head_dim);
   if (p.rc) return p.rc;
   if (p.ws_bytes > 0) {
     if (!workspace || workspace_bytes < p.ws_bytes)
@@ -388,7 +437,7 @@ int decode_common(const void* q, mqa_dtype q_dtype, float* out, const void* k_ne
   ptrs.ws = p.ws_bytes ? static_cast<float*>(workspace) : nullptr;
   ptrs.k_new = k_new;
   ptrs.v_new = v_new;
-  hipError_t e = launch_decode(pool->head_dim, q_dtype == MQA_F32, p.nrt, nk, a, ptrs,
+  hipError_t e = launch_decode(pool->head_dim, q_dtype == MQA_F32, p.nrt, p.waves, nk, a, ptrs,
                                static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, what);
   return ok();

@@ -738,13 +738,16 @@ __device__ __forceinline__ float ld_dev(const float* p) {
 // the output (the workgroup covered the whole key range) or publish a partial
 // record, count the arrival, and let the chunk that arrives last fold every
 // chunk's record in chunk order and write the output.
-template <int D, int QS, int NRT, NewKV NK>
-__global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(
+// W wavefronts per workgroup: 8 (one workgroup per CU), or 4 (two per CU, so
+// that launches with few items fill more of the chip); two wavefronts per SIMD
+// either way, which the launch bound's second argument states for W = 4.
+template <int D, int QS, int NRT, NewKV NK, int W>
+__global__ __launch_bounds__(W * 64, 2) void decode_kernel(
     const DecodeArgs a, const void* __restrict__ qp, float* __restrict__ out,
     uint8_t* __restrict__ pool, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ context_lens, float* __restrict__ ws,
     const void* __restrict__ k_new, const void* __restrict__ v_new) {
-  constexpr int W = kDecodeWaves, RB = kDecodeRing;
+  constexpr int RB = kDecodeRing;
   constexpr int VT = Geo<D>::VT;
   constexpr int PAIRS = NRT * VT;             // (row tile, channel tile) pairs of the output
   constexpr int PPW = (PAIRS + W - 1) / W;    // pairs per wavefront in the merge
@@ -1005,8 +1008,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(
   // ---- this wavefront's pairs over all chunks, folded in chunk order ----
   // (the order, not the arrival, fixes the rounding: results are deterministic)
   // Records are loaded only for chunks that exist, CB per round trip; this
-  // wavefront's own chunk comes from its registers (the same values).
-  constexpr int CB = 8;
+  // wavefront's own chunk comes from its registers (the same values).  With
+  // four pairs per wavefront, eight records per round trip would not fit the
+  // registers.
+  constexpr int CB = PPW >= 4 ? 4 : 8;
   float M[PPW], L[PPW];
   f32x4 A[PPW];
 #pragma unroll
@@ -1243,25 +1248,32 @@ __global__ __launch_bounds__(kAppendWaves * 64) void append_kernel(
 // ---------------------------------------------------------------------------
 static inline dim3 padded_grid(int total) { return dim3((unsigned)((total + 7) / 8 * 8)); }
 
-template <int D, int QS, int NRT, NewKV NK>
+template <int D, int QS, int NRT, NewKV NK, int W>
 static hipError_t launch_decode_t(const DecodeArgs& a, const DecodePtrs& p, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<D, QS, NRT, NK>), padded_grid(a.total_wgs),
-                     dim3(kDecodeWaves * 64), 0, stream, a, p.q, p.out, p.pool, p.block_table,
-                     p.context_lens, p.ws, p.k_new, p.v_new);
+  hipLaunchKernelGGL((decode_kernel<D, QS, NRT, NK, W>), padded_grid(a.total_wgs), dim3(W * 64), 0,
+                     stream, a, p.q, p.out, p.pool, p.block_table, p.context_lens, p.ws, p.k_new,
+                     p.v_new);
   return hipGetLastError();
 }
 
-template <int D, int QS, int NRT>
-static hipError_t launch_decode_n(NewKV nk, const DecodeArgs& a, const DecodePtrs& p,
+template <int D, int QS, int NRT, int W>
+static hipError_t launch_decode_w(NewKV nk, const DecodeArgs& a, const DecodePtrs& p,
                                   hipStream_t stream) {
-  if (nk == NewKV::kBf16) return launch_decode_t<D, QS, NRT, NewKV::kBf16>(a, p, stream);
-  if (nk == NewKV::kF32) return launch_decode_t<D, QS, NRT, NewKV::kF32>(a, p, stream);
-  return launch_decode_t<D, QS, NRT, NewKV::kNone>(a, p, stream);
+  if (nk == NewKV::kBf16) return launch_decode_t<D, QS, NRT, NewKV::kBf16, W>(a, p, stream);
+  if (nk == NewKV::kF32) return launch_decode_t<D, QS, NRT, NewKV::kF32, W>(a, p, stream);
+  return launch_decode_t<D, QS, NRT, NewKV::kNone, W>(a, p, stream);
 }
 
-hipError_t launch_decode(int D, bool q_f32, int nrt, NewKV nk, const DecodeArgs& a,
+template <int D, int QS, int NRT>
+static hipError_t launch_decode_n(int waves, NewKV nk, const DecodeArgs& a, const DecodePtrs& p,
+                                  hipStream_t stream) {
+  if (waves == kDecodeWavesSmall) return launch_decode_w<D, QS, NRT, kDecodeWavesSmall>(nk, a, p, stream);
+  return launch_decode_w<D, QS, NRT, kDecodeWaves>(nk, a, p, stream);
+}
+
+hipError_t launch_decode(int D, bool q_f32, int nrt, int waves, NewKV nk, const DecodeArgs& a,
                          const DecodePtrs& p, hipStream_t stream) {
-#define MQA_DEC(DD, QQ, NN) return launch_decode_n<DD, QQ, NN>(nk, a, p, stream)
+#define MQA_DEC(DD, QQ, NN) return launch_decode_n<DD, QQ, NN>(waves, nk, a, p, stream)
   if (D == 128) {
     if (q_f32) { if (nrt == 1) MQA_DEC(128, 2, 1); MQA_DEC(128, 2, 2); }
     if (nrt == 1) MQA_DEC(128, 1, 1);

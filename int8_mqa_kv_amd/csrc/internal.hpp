@@ -115,7 +115,7 @@ hipError_t launch_pack(int D, bool bf16, const void* k, const void* v, int64_t n
                        int64_t row_stride, const int64_t* slot_mapping, uint8_t* pool,
                        int64_t num_pages, hipStream_t stream);
 
-hipError_t launch_decode(int D, bool q_f32, int nrt, NewKV new_kv, const DecodeArgs& a,
+hipError_t launch_decode(int D, bool q_f32, int nrt, int waves, NewKV new_kv, const DecodeArgs& a,
                          const DecodePtrs& p, hipStream_t stream);
 
 hipError_t launch_append(int D, bool q_f32, int nrt, const AppendArgs& a, const AppendPtrs& p,
@@ -136,7 +136,8 @@ constexpr int64_t ws_record_floats(int D) { return (int64_t)2 * (D / 16) * kPair
 constexpr int64_t kDecodeCounters = 65536;        // arrival counters per call, at most
 constexpr int64_t kCounterStride = 32;            // 32-bit words per counter (128 bytes)
 constexpr int64_t kCounterWords = kDecodeCounters * kCounterStride;  // 8 MiB prefix
-constexpr int kDecodeWaves = 8;     // wavefronts per decode workgroup
+constexpr int kDecodeWaves = 8;     // wavefronts per decode workgroup (one workgroup per CU)
+constexpr int kDecodeWavesSmall = 4;  // the two-per-CU shape for launches with few items
 constexpr int kDecodeRing = 2;      // blocks of two pages in flight per wavefront
 
 }  // namespace mqa

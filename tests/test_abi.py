@@ -114,6 +114,42 @@ def test_decode_workspace_sizes():
     assert ws1 >= 0
 
 
+def _ws_with_waves(args, waves):
+    mk.decode_tuning(waves=waves)
+    try:
+        return mk.decode_workspace_bytes(*args)
+    finally:
+        mk.decode_tuning()
+
+
+def test_decode_workgroup_shape_choice():
+    """Four-wavefront workgroups (two per CU) only where eight leave CUs idle.
+    The choice shows in the workspace size: the two shapes split items into
+    different chunk counts, so they need different numbers of partial records."""
+    three_layers_one_slot = (32, 32, [0, 0, 0], [0, 0, 0], 16384, 128)  # 96 items: 192 of 256 CUs
+    ragged_130 = (130, 32, [0], [0], 1500, 128)                        # 130 items, one chunk each
+    local_64 = (64, 32, [0], [1024], 4096, 128)                         # 128 items x 2 chunks
+    global_16 = (16, 32, [0], [0], 32768, 128)                          # 16 items x 16 chunks
+    for args in (three_layers_one_slot, ragged_130):
+        auto = mk.decode_workspace_bytes(*args)
+        assert auto == _ws_with_waves(args, 4) != _ws_with_waves(args, 8), args
+    for args in (local_64, global_16):
+        auto = mk.decode_workspace_bytes(*args)
+        assert auto == _ws_with_waves(args, 8) != _ws_with_waves(args, 4), args
+    # 96 items: 2 chunks of 8 wavefronts or 5 of 4 (partial records of 16 pairs x 288 fp32)
+    rec = 16 * 288 * 4
+    assert _ws_with_waves(three_layers_one_slot, 8) == (8 << 20) + 96 * 2 * rec
+    assert _ws_with_waves(three_layers_one_slot, 4) == (8 << 20) + 96 * 5 * rec
+
+
+@pytest.mark.parametrize("kw", [dict(waves=6), dict(waves=-4), dict(rows=24), dict(target_wgs=-1)])
+def test_decode_tuning_rejects_bad_values(kw):
+    before = mk.decode_workspace_bytes(32, 32, [0, 0, 0], [0, 0, 0], 16384, 128)
+    with pytest.raises(mk.MQAError):
+        mk.decode_tuning(**kw)
+    assert mk.decode_workspace_bytes(32, 32, [0, 0, 0], [0, 0, 0], 16384, 128) == before
+
+
 def test_pack_rejects_bad_arguments():
     rc = mk.lib.kv_pack_int8(0x1000, 0x2000, 5, 4, 128, 0x3000, ctypes.byref(_pool()), None)
     assert rc == mk.MQA_ERR_UNSUPPORTED
