@@ -14,7 +14,11 @@ Inputs are rotated over replicas (pool, q, out, new rows) whose attended bytes
 together exceed 1 GB, so the 256 MB Infinity Cache and the L2s cannot serve a
 step from the previous one.  By default the steps are replayed from HIP graphs
 (one step per replica per graph), as a serving loop replays its captured
-decode step; HIP events on the replay stream time the region.  The roofline's
+decode step; HIP events on the replay stream time the region.  Before each
+timed region its graph is replayed untimed for --settle-ms (default 300 ms):
+the GPU runs its first fraction of a second of sustained load slower (case 3
+measured 65 -> 58 -> 55 us per step over successive timed regions without it),
+and a serving loop runs in the settled state.  The roofline's
 launch duration is that of the dominant kernel: the decode step's single
 kernel (so the step time), or for the append case the attention call timed
 alone from a graph of only those calls.  --no-graph launches every call from
@@ -279,6 +283,18 @@ def time_graphs(w, st, R, reps, mk, torch, args):
         g.replay()
     torch.cuda.synchronize()
 
+    def settle(g):
+        """Untimed replays for args.settle_ms of wall time (at least one),
+        synchronising every few so the queue stays short."""
+        end = time.perf_counter() + args.settle_ms * 1e-3
+        n = 0
+        while n == 0 or time.perf_counter() < end:
+            g.replay()
+            n += 1
+            if n % 4 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+
     def timed(gf, gr):
         E = torch.cuda.Event
         t0, t1 = E(enable_timing=True), E(enable_timing=True)
@@ -292,7 +308,10 @@ def time_graphs(w, st, R, reps, mk, torch, args):
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / args.steps
 
-    return timed(g_full, g_rem), timed(a_full, a_rem)
+    settle(g_full)
+    t_step = timed(g_full, g_rem)
+    settle(a_full)
+    return t_step, timed(a_full, a_rem)
 
 
 # --------------------------------------------------------------------------
@@ -311,6 +330,8 @@ def main():
                     help="turn rocprofv3 --pmc runs in DIR into profiles/attention_counters_caseN.json")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch every step from the host instead of replaying HIP graphs")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed replays of each graph before its timed region (ms of wall time)")
     args = ap.parse_args()
 
     if args.copy_probe:
@@ -384,7 +405,8 @@ def main():
     if w.kind == "decode" and not args.no_graph:
         roof["attention_only_us"] = round(attn_ms * 1e3, 3)
     roof["timing"] = ("host launches, events around each call" if args.no_graph else
-                      "HIP graph replay of back-to-back calls, events around the replays")
+                      f"HIP graph replay of back-to-back calls after {args.settle_ms:g} ms of untimed "
+                      "replays, events around the timed replays")
     roof["traffic"] = traffic_from_profile(w.case, kv_bytes)
     res["roofline"] = roof
     res["memory"] = memory_report(w, mk)
