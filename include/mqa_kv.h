@@ -170,8 +170,9 @@ size_t mqa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
  * for "the planner decides" or a forced value:
  *  waves       wavefronts per decode workgroup: 8 (one workgroup per CU) or
  *              4 (two per CU).  The planner takes 4 only when the 8-wavefront
- *              plan leaves more than 15 % of the CUs idle and 4 fills at
- *              least 10 % more of the slots with at most 8 chunks per item.
+ *              plan leaves more than 15 % of the CUs idle while splitting
+ *              every item into at least 2 chunks, and 4 fills at least 10 %
+ *              more of the slots with at most 8 chunks per item.
  *  rows        query rows per row block: 8, 16 or 32.
  *  target_wgs  workgroups of 8 wavefronts the planner aims for (default 256,
  *              one per CU of an MI355X).

@@ -282,9 +282,12 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
 
 // The workgroup shape of a launch.  Eight wavefronts per workgroup, one
 // workgroup per CU, unless that plan leaves more than 15 % of the CUs idle
-// (few items, each split into whole chunks) and four-wavefront workgroups, two
-// per CU, fill at least 10 % more of the slots with at most 8 chunks per item
-// (the last arrival folds every chunk's record).
+// (few items, each split into whole chunks) while already splitting every
+// item into at least two chunks, and four-wavefront workgroups, two per CU,
+// fill at least 10 % more of the slots with at most 8 chunks per item (the
+// last arrival folds every chunk's record).  An item the eight-wavefront plan
+// keeps whole needs no handoff between workgroups; splitting it to fill the
+// chip measured slower (short ranges are bound by latency, not by the loop).
 DecodePlan plan_decode_auto(int32_t batch, int32_t num_q_heads, int32_t num_layers,
                             const int32_t* layer_slot, const int32_t* layer_window,
                             int32_t max_context, int32_t head_dim) {
@@ -297,6 +300,8 @@ DecodePlan plan_decode_auto(int32_t batch, int32_t num_q_heads, int32_t num_laye
   const double slots = target_workgroups();
   const double fill8 = p8.args.total_wgs / slots;
   if (fill8 >= 0.85) return p8;
+  for (int g = 0; g < p8.args.num_groups; ++g)
+    if (p8.args.groups[g].nchunk < 2) return p8;
   DecodePlan p4 = plan_decode(batch, num_q_heads, num_layers, layer_slot, layer_window,
                               max_context, head_dim, kDecodeWavesSmall);
   if (p4.rc) {

@@ -123,17 +123,17 @@ def _ws_with_waves(args, waves):
 
 
 def test_decode_workgroup_shape_choice():
-    """Four-wavefront workgroups (two per CU) only where eight leave CUs idle.
-    The choice shows in the workspace size: the two shapes split items into
-    different chunk counts, so they need different numbers of partial records."""
-    three_layers_one_slot = (32, 32, [0, 0, 0], [0, 0, 0], 16384, 128)  # 96 items: 192 of 256 CUs
-    ragged_130 = (130, 32, [0], [0], 1500, 128)                        # 130 items, one chunk each
+    """Four-wavefront workgroups (two per CU) only where eight leave CUs idle
+    while already splitting every item.  The choice shows in the workspace
+    size: the two shapes split items into different chunk counts, so they need
+    different numbers of partial records."""
+    three_layers_one_slot = (32, 32, [0, 0, 0], [0, 0, 0], 16384, 128)  # 96 items x 2: 192 of 256 CUs
+    ragged_130 = (130, 32, [0], [0], 1500, 128)                        # 130 items, kept whole
     local_64 = (64, 32, [0], [1024], 4096, 128)                         # 128 items x 2 chunks
     global_16 = (16, 32, [0], [0], 32768, 128)                          # 16 items x 16 chunks
-    for args in (three_layers_one_slot, ragged_130):
-        auto = mk.decode_workspace_bytes(*args)
-        assert auto == _ws_with_waves(args, 4) != _ws_with_waves(args, 8), args
-    for args in (local_64, global_16):
+    auto = mk.decode_workspace_bytes(*three_layers_one_slot)
+    assert auto == _ws_with_waves(three_layers_one_slot, 4) != _ws_with_waves(three_layers_one_slot, 8)
+    for args in (ragged_130, local_64, global_16):
         auto = mk.decode_workspace_bytes(*args)
         assert auto == _ws_with_waves(args, 8) != _ws_with_waves(args, 4), args
     # 96 items: 2 chunks of 8 wavefronts or 5 of 4 (partial records of 16 pairs x 288 fp32)

@@ -25,7 +25,7 @@ def waves(request):
 WORKLOADS = {
     # 96 row-block items over one shared slot, 16k tokens each
     "three_layers_one_slot": lambda: synth.case3(),
-    # 130 ragged sequences: one chunk each with eight wavefronts, three with four
+    # 130 ragged sequences: kept whole with eight wavefronts, three chunks with four
     "ragged_130": lambda: synth.custom_decode(
         22, 130, 32, 128, "bf16", [1 + (37 * i * i + 11 * i) % 1500 for i in range(130)], 1, 0, 0),
     # windowed layer, contexts from 1 to 12345 tokens, permuted pool
