@@ -1,7 +1,9 @@
 """Both decode workgroup shapes -- eight wavefronts (one workgroup per CU) and
 four (two per CU) -- forced in turn through the same workloads, against the
-oracle.  Which shape a launch takes by default is a planner choice (tested on
-the CPU); each must compute the same attention within the usual tolerance.
+oracle, and the other plans mqa_decode_tuning allows (8-, 16- and 32-row
+blocks, workgroup targets from 64 to 1024).  Which plan a launch takes by
+default is a planner choice (tested on the CPU); each must compute the same
+attention within the usual tolerance.
 """
 import pytest
 
@@ -50,3 +52,24 @@ def test_step_shape(waves):
     w = synth.custom_decode(40, 5, 32, 128, "bf16", [1, 16, 17, 1500, 3001], 4, 0,
                             permuted_pool=800)
     check_step(w, [0, 0, 0, 0], [0, 1024, 1, 300])
+
+
+# Plans the planner does not pick by itself but mqa_decode_tuning allows:
+# 8-row blocks, and workgroup targets far below and above one per CU (fewer,
+# longer chunks; several rounds of workgroups).
+TUNINGS = [dict(rows=8), dict(rows=16), dict(rows=32), dict(target_wgs=64), dict(target_wgs=1024),
+           dict(waves=4, rows=8)]
+
+
+@pytest.fixture(params=TUNINGS, ids=["-".join(f"{k}{v}" for k, v in t.items()) for t in TUNINGS])
+def tuning(request):
+    mk.decode_tuning(**request.param)
+    try:
+        yield request.param
+    finally:
+        mk.decode_tuning()
+
+
+@pytest.mark.parametrize("name", ["window_ragged", "heads48", "d64"])
+def test_decode_tuned_plan(tuning, name):
+    _run_case(WORKLOADS[name]())
