@@ -345,7 +345,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
-              f"{world}); the multi-GPU sharding is described in DESIGN.md, not run.",
+              f"{world}); the library runs on one GPU per process, and no sharding across GPUs is built.",
               file=sys.stderr)
         sys.exit(2)
 

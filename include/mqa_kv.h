@@ -60,7 +60,7 @@ extern "C" {
 typedef enum {
   MQA_OK = 0,
   MQA_ERR_INVALID = -1,      /* a bad argument                                  */
-  MQA_ERR_UNSUPPORTED = -2,  /* a valid request this build does not implement   */
+  MQA_ERR_UNSUPPORTED = -2,  /* a valid request this library does not implement */
   MQA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required      */
   MQA_ERR_HIP = -4           /* the HIP runtime reported an error               */
 } mqa_status;

@@ -18,7 +18,7 @@ What it computes (the pages, cited by title and section):
 * "Como funciona a inferência de IA", section "Qual é o tamanho real do cache
   KV?": bytes per token = 2 x layers x kv_heads x head_dim x dtype bytes.
 
-Readings where the pages are silent (each also listed in the design doc): the
+Readings where the pages are silent: the
 softmax scale is 1/sqrt(head_dim); the quantiser is symmetric per token with an
 fp32 scale max|x|/127, codes rint(x/s) rounded half to even and clamped to
 +-127; a window W covers the query's own position and the W-1 before it; the
