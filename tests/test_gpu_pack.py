@@ -111,3 +111,30 @@ def test_pack_skips_negative_slots_and_respects_stride():
     assert np.array_equal(kc, okc) and np.array_equal(ks, oks)
     # pages 2 and 3 were never addressed
     assert np.all(data[2:] == 0x5A)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_pack_near_ties_match_golden_codes(d):
+    """The near-tie rows derived with exact rationals from the quantiser's
+    definition (tests/golden/quantiser_near_ties.json): the kernel's codes and
+    scale bits equal the file's, not only the oracle's."""
+    log(f"pack near-tie golden rows d={d}")
+    g = json.load(open(os.path.join(GOLDEN, "quantiser_near_ties.json")))
+    rows, want, scales = [], [], []
+    for r in g["rows"]:
+        x = np.zeros(d, np.float32)
+        vals = np.array([int(h, 16) for h in r["x_bits"]], np.uint32).view(np.float32)
+        x[:len(vals)] = vals
+        rows.append(x)
+        c = np.zeros(d, np.int8)
+        c[:len(vals)] = r["codes"]
+        want.append(c)
+        scales.append(int(r["scale_bits"], 16))
+    k = np.stack(rows)
+    v = -k[::-1].copy()
+    kc, ks, vc, vs = _pack_and_read(k, v, d, "f32", perm_seed=9)
+    want = np.stack(want)
+    assert np.array_equal(kc, want), f"K codes differ in {int((kc != want).sum())} places"
+    assert np.array_equal(vc, -want[::-1]), "V codes differ"
+    assert ks.view(np.uint32).tolist() == scales
+    assert vs.view(np.uint32).tolist() == scales[::-1]

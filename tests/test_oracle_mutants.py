@@ -36,6 +36,10 @@ MUTANTS = [
     ("quantiser rounds half away from zero", "float n = nearbyintf(r);",
      "float n = roundf(r);"),
     ("quantiser truncates", "float n = nearbyintf(r);", "float n = truncf(r);"),
+    ("quantiser multiplies by a reciprocal of the scale", "volatile float r = row[c] / sv;",
+     "volatile float r = row[c] * (1.0f / sv);"),
+    ("quantiser multiplies by 127 / max", "volatile float r = row[c] / sv;",
+     "volatile float r = row[c] * (127.0f / a);"),
     ("dequantiser drops the scale",
      "(double)scales[t] * (double)codes[t * (int64_t)d + c];",
      "(double)codes[t * (int64_t)d + c];"),

@@ -67,6 +67,39 @@ def test_quantiser_golden_ties():
         assert codes[0].tolist() == row["codes"]
 
 
+def _bits_to_f32(hexes):
+    return np.array([int(h, 16) for h in hexes], dtype=np.uint32).view(np.float32)
+
+
+def test_quantiser_near_ties_fix_the_division():
+    """Near ties of x / s derived with exact rationals (make_quantiser_near_ties.py):
+    the codes of fl32(x / s) differ there from those of x * fl32(1 / s) and of
+    x * fl32(127 / a), so only a quantiser that divides passes."""
+    g = json.load(open(os.path.join(GOLDEN, "quantiser_near_ties.json")))
+    assert len(g["rows"]) >= 4
+    n_rec = n_inv = 0
+    for row in g["rows"]:
+        x = _bits_to_f32(row["x_bits"])[None, :]
+        codes, scales = oracle.quantize(x)
+        assert scales.view(np.uint32)[0] == int(row["scale_bits"], 16)
+        assert codes[0].tolist() == row["codes"]
+        n_rec += sum(a != b for a, b in zip(row["codes"], row["codes_if_reciprocal"]))
+        n_inv += sum(a != b for a, b in zip(row["codes"], row["codes_if_inverse_scale"]))
+    # the file really separates the three forms
+    assert n_rec > 0 and n_inv > 0
+
+
+def test_bf16_bit_patterns():
+    """bfloat16 is the top half of an fp32 pattern: fixed values of the format."""
+    bits = np.array([0x3F80, 0xC040, 0x0001, 0x7F7F, 0x8000, 0x4049, 0x0080], dtype=np.uint16)
+    got = oracle.bf16_bits_to_f64(bits)
+    want = [1.0, -3.0, 2.0 ** -133, (2.0 - 2.0 ** -7) * 2.0 ** 127, -0.0,
+            3.140625, 2.0 ** -126]
+    assert got.dtype == np.float64
+    for g_, w_ in zip(got.tolist(), want):
+        assert g_ == w_ and math.copysign(1, g_) == math.copysign(1, w_)
+
+
 def test_quantiser_error_bound_and_range():
     x = _rows(1, 4000, 128) * np.float32(3.0)
     codes, s = oracle.quantize(x)
