@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Throughput of the int8 MQA KV attention path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--case 1|2|3|4] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--case 1|2|3|4] [--extra-cases 1,2,4] [--gpus 1]
 
 One step is one pass of the whole hot path over one batch of synthetic input
 already resident in HBM:
@@ -10,20 +10,26 @@ already resident in HBM:
                       every layer of the case, in one launch;
   append case (4):    kv_pack_int8 of the appended chunk into every slot, then
                       mqa_append_attn over all 12 layers.
-Inputs are rotated over replicas (pool, q, out, new rows) whose attended bytes
-together exceed 1 GB, so the 256 MB Infinity Cache and the L2s cannot serve a
-step from the previous one.  By default the steps are replayed from HIP graphs
-(one step per replica per graph), as a serving loop replays its captured
-decode step; HIP events on the replay stream time the region.  Before each
-timed region its graph is replayed untimed for --settle-ms (default 300 ms):
-the GPU runs its first fraction of a second of sustained load slower (case 3
-measured 65 -> 58 -> 55 us per step over successive timed regions without it),
-and a serving loop runs in the settled state.  The roofline's
-launch duration is that of the dominant kernel: the decode step's single
-kernel (so the step time), or for the append case the attention call timed
-alone from a graph of only those calls.  --no-graph launches every call from
-the host instead (then the host's launch rate, not the GPU, limits the small
-cases).
+The headline line is case 3 (three global layers reading one shared slot,
+32 sequences at 16k context: the largest decode workload); the other cases
+are timed in the same run and reported under "workloads", each with its own
+roofline, counter traffic and CPU baseline.  Inputs are rotated over replicas
+(pool, q, out, new rows) whose attended bytes together exceed 1 GB, so the
+256 MB Infinity Cache and the L2s cannot serve a step from the previous one.
+By default the steps are replayed from HIP graphs (one step per replica per
+graph), as a serving loop replays its captured decode step; HIP events on
+the replay stream time the region.  Before each timed region its graph is
+replayed untimed for --settle-ms (default 300 ms): the GPU runs its first
+fraction of a second of sustained load slower (case 3 measured 65 -> 58 ->
+55 us per step over successive timed regions without it), and a serving
+loop runs in the settled state.  The roofline's launch duration is that of
+the dominant kernel: the decode step's single kernel (so the step time), or
+for the append case the attention call timed alone from a graph of only
+those calls.  --no-graph launches every call from the host instead (then the
+host's launch rate, not the GPU, limits the small cases).
+
+A streaming-read probe (mqa_hbm_read_probe) reports the HBM bandwidth a plain
+read reaches on this GPU, beside the published 8 TB/s.
 
 Prints one JSON line.  ``value`` is int8 KV GB/s of the whole step: the KV
 bytes the step must stream (codes + fp32 scales of every attended key of every
@@ -138,7 +144,7 @@ def setup(w, replicas, torch, mk, synth):
     ws = None
     if w.kind == "decode":
         wsb = mk.decode_workspace_bytes(w.batch, w.num_q_heads, w.layer_slot, w.layer_window,
-                                        w.max_context, w.head_dim)
+                                        w.max_context, w.head_dim, w.q_dtype)
         ws = torch.zeros(max(wsb, 256), dtype=torch.uint8, device=dev) if wsb else None
     torch.cuda.synchronize()
     return dict(bt=bt, ctx=ctx, cu=cu, sm=new_sm, reps=reps, ws=ws)
@@ -230,8 +236,18 @@ def cpu_baseline(w, kv_bytes_step, budget_s):
               f"{n} pass(es) over {len(seqs)} of {w.batch} sequences, scaled to the whole step")
     return {"value": kv_bytes_step / per_step / 1e9, "unit": "GB/s",
             "cores": oracle.num_threads(), "kind": "oracle", "sample": sample,
-            "seconds": round(el, 3), "s_per_step": per_step,
-            "cpu": platform.processor() or platform.machine()}
+            "seconds": round(el, 3), "s_per_step": per_step, "cpu": cpu_model()}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (as lscpu prints it), from /proc/cpuinfo."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def time_eager(w, st, R, reps, mk, torch, args):
@@ -315,15 +331,147 @@ def time_graphs(w, st, R, reps, mk, torch, args):
 
 
 # --------------------------------------------------------------------------
+def measure_case(case, args, torch, mk, synth, headline):
+    """Set up, time and report one workload; frees its GPU memory after."""
+    t_setup = time.perf_counter()
+    w = synth.case(case)
+    kv_bytes = w.attended_keys() * (2 * w.head_dim + 8)
+    reps = args.replicas or max(1, math.ceil(1.0e9 / kv_bytes))
+    if w.kind == "append":
+        reps = args.replicas or 1   # footprint is several GB already
+    log(f"case {w.case}: {w.name}; KV bytes/step {kv_bytes}; replicas {reps}")
+    st = setup(w, reps, torch, mk, synth)
+    R = st["reps"]
+    log(f"  set-up {time.perf_counter() - t_setup:.1f} s")
+    steps = args.steps if headline else args.extra_steps
+    a = argparse.Namespace(**vars(args))
+    a.steps = steps
+
+    if args.no_graph:
+        ms_step, attn_ms = time_eager(w, st, R, reps, mk, torch, a)
+    else:
+        ms_step, attn_ms = time_graphs(w, st, R, reps, mk, torch, a)
+    log(f"  step {ms_step * 1e3:.2f} us, attention call {attn_ms * 1e3:.2f} us")
+    # the dominant kernel: the decode step is one kernel, so its launch time
+    # is the step time; for append it is the attention call
+    # (host launches: the events around each step's kernel)
+    dom_ms = ms_step if (w.kind == "decode" and not args.no_graph) else attn_ms
+
+    tokens = int(w.q_lens.sum()) * w.num_layers
+    value = kv_bytes / (ms_step * 1e-3) / 1e9
+    res = {
+        "steps": steps, "ms_per_step": round(ms_step, 6),
+        "config": {"workload": f"case {w.case}: {w.name}", "batch": w.batch,
+                   "num_q_heads": w.num_q_heads, "kv_heads": 1, "head_dim": w.head_dim,
+                   "layers": w.num_layers, "layer_window": w.layer_window.tolist(),
+                   "max_context": w.max_context, "q_dtype": w.q_dtype,
+                   "parallelism": "none (1 GPU)", "replicas": reps},
+        "value": round(value, 2), "unit": "GB/s",
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "decode_tokens_per_s" if w.kind == "decode" else "appended_tokens_per_s":
+            round(tokens / (ms_step * 1e-3), 1),
+        "kv_bytes_per_step": kv_bytes,
+    }
+    if w.kind == "decode":
+        achieved = kv_bytes / (dom_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        fl = attention_flops(w)
+        achieved = fl / (dom_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4)}
+    roof["kernel"] = ("decode_kernel (mqa_decode_step: store + attention, one launch)"
+                      if w.kind == "decode" else "append_kernel (mqa_append_attn)")
+    roof["avg_launch_us"] = round(dom_ms * 1e3, 3)
+    if w.kind == "decode" and not args.no_graph:
+        roof["attention_only_us"] = round(attn_ms * 1e3, 3)
+    roof["timing"] = ("host launches, events around each call" if args.no_graph else
+                      f"HIP graph replay of back-to-back calls after {args.settle_ms:g} ms of untimed "
+                      "replays, events on the replay stream around the timed replays")
+    roof["traffic"] = traffic_from_profile(w.case, kv_bytes)
+    res["roofline"] = roof
+    res["memory"] = memory_report(w, mk)
+    if w.kind == "decode" and not args.no_graph and w.num_layers == 1:
+        log("  grouped-query bf16 baseline on the same step ...")
+        res["gqa8_bf16_baseline"] = gqa_report(w, mk, torch, ms_step)
+    if w.kind == "append":
+        log("  prefix cache: offload and restore of the cached prefixes ...")
+        res["memory"]["prefix_cache"] = prefix_restore_report(w, st, mk, torch)
+    del st, R
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("  timing the oracle on the host cores ...")
+        budget = args.cpu_seconds if headline else args.extra_cpu_seconds
+        res["cpu_baseline"] = cpu_baseline(w, kv_bytes, budget)
+    return res
+
+
+def hbm_probe(torch, mk, sizes, total=2 << 30, launches=40):
+    """mqa_hbm_read_probe over a 2 GiB buffer: each launch reads a fresh slice
+    of ``size`` bytes (slices rotate through the buffer, so neither the L2s
+    nor the 256 MB Infinity Cache hold a slice from an earlier launch);
+    launches are replayed from a HIP graph and timed with events on the
+    replay stream.  Returns GB/s per size."""
+    buf = torch.empty(total, dtype=torch.uint8, device="cuda")
+    buf.random_(0, 256)
+    sink = torch.zeros(mk.PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
+    out = {}
+    for size in sizes:
+        size = min(int(size) // 4096 * 4096, total)
+        n = max(1, total // size)
+        views = [buf[i * size:(i + 1) * size] for i in range(n)]
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for v in views:
+                mk.hbm_read_probe(v, sink)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        per = max(1, launches // n)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(per):
+                for v in views:
+                    mk.hbm_read_probe(v, sink)
+        g.replay()
+        torch.cuda.synchronize()
+        E = torch.cuda.Event
+        e0, e1 = E(enable_timing=True), E(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) * 1e-3 / (per * n)
+        out[str(size)] = {"bytes": size, "us_per_read": round(sec * 1e6, 3),
+                          "gbs": round(size / sec / 1e9, 1),
+                          "pct_of_8000": round(100 * size / sec / 1e9 / HBM_PEAK_GBS, 2)}
+    # the probe's own check: the XOR of the sink words is that of the buffer
+    mk.hbm_read_probe(buf[:1 << 20], sink)
+    got = int(np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)))
+    want = int(np.bitwise_xor.reduce(buf[:1 << 20].cpu().numpy().view(np.uint32)))
+    del buf, sink
+    torch.cuda.empty_cache()
+    return {"kernel": "hbm_read_kernel (mqa_hbm_read_probe): 128-bit loads, 8 in flight per lane",
+            "by_size": out, "xor_check": got == want}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--case", type=int, default=1, choices=[1, 2, 3, 4])
+    ap.add_argument("--case", type=int, default=3, choices=[1, 2, 3, 4],
+                    help="the headline workload (default 3, the largest decode case)")
+    ap.add_argument("--extra-cases", default="1,2,4",
+                    help="other cases timed in the same run ('' for none)")
+    ap.add_argument("--extra-steps", type=int, default=100)
     ap.add_argument("--replicas", type=int, default=0, help="0: enough for >= 1 GB of KV")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--extra-cpu-seconds", type=float, default=4.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true", help="skip the HBM streaming-read probe")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB copy (counter calibration) and exit")
     ap.add_argument("--summarize-counters", metavar="DIR",
@@ -353,72 +501,26 @@ def main():
     import int8_mqa_kv_amd as mk
     import synth
 
-    w = synth.case(args.case)
-    kv_bytes = w.attended_keys() * (2 * w.head_dim + 8)
-    reps = args.replicas or max(1, math.ceil(1.0e9 / kv_bytes))
-    if w.kind == "append":
-        reps = args.replicas or 1   # footprint is several GB already
-    log(f"case {w.case}: {w.name}; KV bytes/step {kv_bytes}; replicas {reps}")
-    st = setup(w, reps, torch, mk, synth)
-    R = st["reps"]
-
-    if args.no_graph:
-        ms_step, attn_ms = time_eager(w, st, R, reps, mk, torch, args)
-    else:
-        ms_step, attn_ms = time_graphs(w, st, R, reps, mk, torch, args)
-    log(f"step {ms_step * 1e3:.2f} us, attention call {attn_ms * 1e3:.2f} us")
-    # the dominant kernel: the decode step is one kernel, so its launch time
-    # is the step time; for append it is the attention call
-    # (host launches: the events around each step's kernel)
-    dom_ms = ms_step if (w.kind == "decode" and not args.no_graph) else attn_ms
-
-    tokens = int(w.q_lens.sum()) * w.num_layers
-    value = kv_bytes / (ms_step * 1e-3) / 1e9
+    extras = [int(c) for c in args.extra_cases.split(",") if c.strip()]
+    extras = [c for c in extras if c != args.case]
+    head = measure_case(args.case, args, torch, mk, synth, headline=True)
     res = {
-        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
+        "metric": METRIC, "value": head.pop("value"), "unit": head.pop("unit"), "n_gpus": 1,
+        "steps": head.pop("steps"), "warmup": args.warmup, "ms_per_step": head.pop("ms_per_step"),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int8",
-        "data": "synthetic (seeded)",
-        "config": {"workload": f"case {w.case}: {w.name}", "batch": w.batch,
-                   "num_q_heads": w.num_q_heads, "kv_heads": 1, "head_dim": w.head_dim,
-                   "layers": w.num_layers, "layer_window": w.layer_window.tolist(),
-                   "max_context": w.max_context, "q_dtype": w.q_dtype,
-                   "parallelism": "none (1 GPU)", "replicas": reps},
-        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "decode_tokens_per_s" if w.kind == "decode" else "appended_tokens_per_s":
-            round(tokens / (ms_step * 1e-3), 1),
-        "kv_bytes_per_step": kv_bytes,
+        "dtype": "int8", "data": "synthetic (seeded)", "config": head.pop("config"),
     }
-    if w.kind == "decode":
-        achieved = kv_bytes / (dom_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    else:
-        fl = attention_flops(w)
-        achieved = fl / (dom_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4)}
-    roof["kernel"] = ("decode_kernel (mqa_decode_step: store + attention, one launch)"
-                      if w.kind == "decode" else "append_kernel (mqa_append_attn)")
-    roof["avg_launch_us"] = round(dom_ms * 1e3, 3)
-    if w.kind == "decode" and not args.no_graph:
-        roof["attention_only_us"] = round(attn_ms * 1e3, 3)
-    roof["timing"] = ("host launches, events around each call" if args.no_graph else
-                      f"HIP graph replay of back-to-back calls after {args.settle_ms:g} ms of untimed "
-                      "replays, events around the timed replays")
-    roof["traffic"] = traffic_from_profile(w.case, kv_bytes)
-    res["roofline"] = roof
-    res["memory"] = memory_report(w, mk)
-    if w.kind == "decode" and not args.no_graph:
-        log("grouped-query bf16 baseline on the same step ...")
-        res["gqa8_bf16_baseline"] = gqa_report(w, mk, torch, ms_step)
-    if w.kind == "append":
-        log("prefix cache: offload and restore of the cached prefixes ...")
-        res["memory"]["prefix_cache"] = prefix_restore_report(w, st, mk, torch)
-    if not args.no_cpu_baseline:
-        log("timing the oracle on the host cores ...")
-        res["cpu_baseline"] = cpu_baseline(w, kv_bytes, args.cpu_seconds)
+    res.update(head)
+    if extras:
+        res["workloads"] = {}
+        for c in extras:
+            res["workloads"][f"case {c}"] = measure_case(c, args, torch, mk, synth, headline=False)
+    if not args.no_probe:
+        log("HBM streaming-read probe ...")
+        sizes = [2 << 30, res["kv_bytes_per_step"]] + [
+            v["kv_bytes_per_step"] for v in res.get("workloads", {}).values()
+            if v["config"]["layers"] == 1]
+        res["hbm_read_probe"] = hbm_probe(torch, mk, sizes)
     print(json.dumps(res), flush=True)
 
 

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MQA_KV_ABI_VERSION 4
+#define MQA_KV_ABI_VERSION 5
 #define MQA_PAGE_TOKENS 16
 
 typedef enum {
@@ -78,10 +78,10 @@ typedef enum {
  * in one record so that one page read brings everything attention needs.
  * Byte positions inside a record are given by mqa_page_offset(); the order is
  * chosen so that each GPU lane's matrix-core operand is one contiguous
- * 16-byte load.  A K code c (-127..127) is stored as the int8 byte c; a V
- * code c is stored as the unsigned byte c + 128 (c with its sign bit
- * flipped), the form the fp16 operand conversion takes as it is.  Pages of every slot come from the same pool; which page
- * holds which tokens is decided by the caller's block tables.
+ * 16-byte load.  A K or V code c (-127..127) is stored as the unsigned
+ * byte c + 128 (c with its sign bit flipped), the form the fp16 operand
+ * conversion takes as it is.  Pages of every slot come from the same pool;
+ * which page holds which tokens is decided by the caller's block tables.
  */
 typedef struct mqa_kv_pool {
   void*   base;
@@ -145,14 +145,16 @@ int kv_pack_int8(const void* k, const void* v, mqa_dtype src_dtype,
 
 /*
  * Workspace for mqa_decode_attn / mqa_decode_step with the same shape
- * arguments (the host arrays are read).  Contexts long enough to be split
- * across workgroups leave softmax partials (max, sum, weighted values) there;
- * the last of them to arrive merges them inside the same kernel.  The first
- * 8 MiB of a workspace hold the arrival counters (one per wavefront of a
- * workgroup, 8 or 4, per 32-head row block of a layer and sequence, each on
- * its own 128-byte line; at most 8192 such pairs per call), the partials
- * follow.  The size depends on the decode tuning in force
- * (mqa_decode_tuning); query it again after changing that.
+ * arguments and query dtype (the host arrays are read).  Contexts long enough
+ * to be split across workgroups leave softmax partials (max, sum, weighted
+ * values) there; the last of them to arrive merges them inside the same
+ * kernel.  The first 8 MiB of a workspace hold the arrival counters (one per
+ * wavefront of a workgroup, 8 or 4, per row block of a layer and sequence,
+ * each on its own 128-byte line; at most 8192 such pairs per call), the
+ * partials follow.  The size depends on the query dtype (fp32 queries are
+ * carried as two fp16 terms, and a wavefront then takes 16 rows instead of
+ * 32) and on the decode tuning in force (mqa_decode_tuning); query it again
+ * after changing that.
  * Returns 0 when none is needed or the arguments are invalid (a following
  * call reports why).  The workspace must be zero-filled ONCE before its first
  * use (e.g. hipMemset after allocation); every call leaves the counters at
@@ -161,7 +163,8 @@ int kv_pack_int8(const void* k, const void* v, mqa_dtype src_dtype,
 size_t mqa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                   int32_t num_layers, const int32_t* layer_slot,
                                   const int32_t* layer_window,
-                                  int32_t max_context, int32_t head_dim);
+                                  int32_t max_context, int32_t head_dim,
+                                  mqa_dtype q_dtype);
 
 /*
  * Decode tuning (not part of what is computed: results depend on it only
@@ -173,7 +176,8 @@ size_t mqa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
  *              plan leaves more than 15 % of the CUs idle while splitting
  *              every item into at least 2 chunks, and 4 fills at least 10 %
  *              more of the slots with at most 8 chunks per item.
- *  rows        query rows per row block: 8, 16 or 32.
+ *  rows        query rows per row block: 8, 16 or 32 (at most 16 with fp32
+ *              queries).
  *  target_wgs  workgroups of 8 wavefronts the planner aims for (default 256,
  *              one per CU of an MI355X).
  * Starts from the environment variables MQA_DECODE_WAVES, MQA_DECODE_ROWS and
@@ -496,6 +500,25 @@ int mqa_prefix_cache_insert_host(mqa_prefix_cache* cache, const int32_t* tokens,
                                  int64_t* cached_pages);
 int mqa_prefix_cache_read_host(const mqa_prefix_cache* cache, const int32_t* tokens,
                                int64_t pages, uint8_t* out, uint64_t* present);
+
+/*
+ * mqa_hbm_read_probe -- a streaming read of device memory, to measure the
+ * bandwidth a plain read reaches on this GPU (decode attention streams KV
+ * bytes, whose volume sets its cost: Character.AI page, section 02).  Not
+ * part of the method.
+ *
+ *  src         device buffer of `bytes` bytes (a positive multiple of 16,
+ *              16-byte aligned), read once with 128-bit loads.
+ *  sink        device uint32 [sink_words], sink_words >= MQA_PROBE_SINK_WORDS.
+ *              Word g (g < MQA_PROBE_SINK_WORDS) receives the XOR of the
+ *              32-bit words of the g-th of MQA_PROBE_SINK_WORDS equal
+ *              contiguous ranges of src (0 for an empty range), so the XOR of
+ *              all sink words equals the XOR of all 32-bit words of src.
+ * Asynchronous on `stream`.  Returns MQA_OK or MQA_ERR_INVALID / MQA_ERR_HIP.
+ */
+#define MQA_PROBE_SINK_WORDS 4096
+int mqa_hbm_read_probe(const void* src, int64_t bytes, uint32_t* sink, int32_t sink_words,
+                       void* stream);
 
 #ifdef __cplusplus
 }

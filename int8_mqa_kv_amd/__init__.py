@@ -37,6 +37,7 @@ __all__ = [
     "mqa_append_attn", "slot_mapping_for", "unpack_page_tokens",
     "kv_footprint_bytes", "PageTable", "PrefixCache",
     "gqa_page_bytes", "gqa_pack_bf16", "gqa_decode_workspace", "gqa_decode_bf16",
+    "PROBE_SINK_WORDS", "hbm_read_probe",
 ]
 
 PAGE_TOKENS = 16
@@ -73,7 +74,7 @@ def _load() -> ctypes.CDLL:
     L.mqa_page_offset.restype = ctypes.c_int
     L.kv_pack_int8.argtypes = [p, p, ctypes.c_int, i64, i64, p, ctypes.POINTER(_Pool), p]
     L.kv_pack_int8.restype = ctypes.c_int
-    L.mqa_decode_workspace_bytes.argtypes = [i32, i32, i32, p, p, i32, i32]
+    L.mqa_decode_workspace_bytes.argtypes = [i32, i32, i32, p, p, i32, i32, ctypes.c_int]
     L.mqa_decode_workspace_bytes.restype = sz
     L.mqa_decode_tuning.argtypes = [i32, i32, i32]
     L.mqa_decode_tuning.restype = ctypes.c_int
@@ -123,6 +124,8 @@ def _load() -> ctypes.CDLL:
     L.mqa_gqa_page_bytes.argtypes, L.mqa_gqa_page_bytes.restype = [i32, i32], sz
     L.mqa_gqa_pack_bf16.argtypes = [p, p, i64, p, p, i64, i32, i32, p]
     L.mqa_gqa_pack_bf16.restype = ctypes.c_int
+    L.mqa_hbm_read_probe.argtypes = [p, i64, p, i32, p]
+    L.mqa_hbm_read_probe.restype = ctypes.c_int
     L.mqa_gqa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     L.mqa_gqa_decode_workspace_bytes.restype = sz
     L.mqa_gqa_decode_bf16.argtypes = [p, p, p, i64, i32, i32, p, i32, p, i32, i32, i32, i32, f32,
@@ -326,6 +329,21 @@ def gqa_page_bytes(num_kv_heads: int, head_dim: int) -> int:
     return n
 
 
+PROBE_SINK_WORDS = 4096
+
+
+def hbm_read_probe(src, sink, stream=None) -> None:
+    """Streaming read of the device tensor ``src`` (``mqa_hbm_read_probe``);
+    ``sink`` uint32-sized (int32) [>= PROBE_SINK_WORDS] receives per-range
+    XORs whose XOR is that of all 32-bit words of ``src``."""
+    torch = _torch()
+    if not src.is_contiguous() or not sink.is_contiguous():
+        raise ValueError("src and sink must be contiguous")
+    _check(lib.mqa_hbm_read_probe(_dev_ptr(src, "src"), src.numel() * src.element_size(),
+                                  _dev_ptr(sink, "sink", torch.int32), int(sink.numel()),
+                                  _stream_ptr(stream)))
+
+
 def gqa_pack_bf16(k, v, slot_mapping, pool, num_kv_heads: int, stream=None) -> None:
     """``k, v`` bf16 [T, Hkv, D]; ``pool`` a uint8 tensor [num_pages, page_bytes]."""
     torch = _torch()
@@ -496,13 +514,27 @@ def kv_pack_int8(k, v, slot_mapping, pool: KVPool, stream=None) -> None:
                             ctypes.byref(pool.c), _stream_ptr(stream)))
 
 
+def _q_dtype_code(q_dtype) -> int:
+    """MQA_BF16 / MQA_F32 from "bf16" / "f32" (or "fp32") or a torch dtype."""
+    t = _torch()
+    if q_dtype in ("bf16", t.bfloat16):
+        return MQA_BF16
+    if q_dtype in ("f32", "fp32", t.float32):
+        return MQA_F32
+    raise ValueError(f"q dtype {q_dtype!r}: bf16 or f32")
+
+
 def decode_workspace_bytes(batch: int, num_q_heads: int, layer_slot: Sequence[int],
-                           layer_window: Sequence[int], max_context: int, head_dim: int) -> int:
+                           layer_window: Sequence[int], max_context: int, head_dim: int,
+                           q_dtype="bf16") -> int:
+    """Workspace bytes (``mqa_decode_workspace_bytes``) of decode calls of these
+    shapes with queries of ``q_dtype``."""
     n = len(layer_slot)
     ls = _host_i32(layer_slot, n, "layer_slot")
     lw = _host_i32(layer_window, n, "layer_window")
     return int(lib.mqa_decode_workspace_bytes(batch, num_q_heads, n, ls.ctypes.data,
-                                              lw.ctypes.data, max_context, head_dim))
+                                              lw.ctypes.data, max_context, head_dim,
+                                              _q_dtype_code(q_dtype)))
 
 
 def decode_tuning(waves: int = 0, rows: int = 0, target_wgs: int = 0) -> None:
@@ -513,11 +545,11 @@ def decode_tuning(waves: int = 0, rows: int = 0, target_wgs: int = 0) -> None:
 
 def decode_workspace(batch: int, num_q_heads: int, layer_slot: Sequence[int],
                      layer_window: Sequence[int], max_context: int, head_dim: int,
-                     device="cuda"):
+                     device="cuda", q_dtype="bf16"):
     """A zero-filled workspace for these decode shapes (None when none is
     needed).  Zero-fill once; every call leaves it reusable."""
     n = decode_workspace_bytes(batch, num_q_heads, layer_slot, layer_window, max_context,
-                               head_dim)
+                               head_dim, q_dtype)
     return _torch().zeros(n, dtype=_torch().uint8, device=device) if n else None
 
 
@@ -628,14 +660,14 @@ def unpack_page_tokens(pool_bytes: np.ndarray, slots: np.ndarray, head_dim: int)
 
     ``pool_bytes`` uint8 [num_pages, page_bytes]; ``slots`` int64 [T]
     (page*16 + offset).  Returns ``(k_codes int8 [T, D], k_scales f32 [T],
-    v_codes int8 [T, D], v_scales f32 [T])``.  A V code c is stored as the
-    byte c + 128 (its sign bit flipped); K codes as plain int8."""
+    v_codes int8 [T, D], v_scales f32 [T])``.  A K or V code c is stored as
+    the byte c + 128 (its sign bit flipped)."""
     k_off, v_off, ks_off, vs_off = page_layout(head_dim)
     slots = np.asarray(slots, dtype=np.int64)
     page, j = slots // PAGE_TOKENS, slots % PAGE_TOKENS
     rec = pool_bytes[page]                                   # [T, page_bytes]
     rows = np.arange(slots.size)[:, None]
-    kc = rec[rows, k_off[j]].view(np.int8)
+    kc = (rec[rows, k_off[j]] ^ np.uint8(0x80)).view(np.int8)
     vc = (rec[rows, v_off[j]] ^ np.uint8(0x80)).view(np.int8)
     ks = np.stack([rec[np.arange(slots.size), ks_off[j] + b] for b in range(4)], 1).copy()
     vs = np.stack([rec[np.arange(slots.size), vs_off[j] + b] for b in range(4)], 1).copy()

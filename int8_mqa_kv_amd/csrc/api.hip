@@ -153,18 +153,22 @@ int decode_rows_override() { return tuning().rows; }
 // between workgroups.  There, 16-row blocks double the workgroups per page
 // (the second reads the pages from L2), halve the chunks each range needs and
 // the size of every partial record, and shorten the handoff.
-int decode_rows(int num_q_heads, int num_layers, int64_t max_span_pages, int64_t items32) {
+// fp32 queries are carried as two fp16 terms per element, which leaves the
+// registers for one 16-row tile per wavefront: 16-row blocks (or 8).
+int decode_rows(int num_q_heads, int num_layers, int64_t max_span_pages, int64_t items32,
+                bool q_f32) {
   int rows = decode_rows_override();
   if (rows == 0)
     rows = (num_q_heads > 16 && max_span_pages <= 128 && 2 * items32 <= target_workgroups())
                ? 16 : kRowsPerBlock;
+  if (q_f32) return std::min(rows, 16);
   if (num_layers * ((num_q_heads + rows - 1) / rows) > kMaxRowBlocks) rows = kRowsPerBlock;
   return rows;
 }
 
 DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
                        const int32_t* layer_slot, const int32_t* layer_window,
-                       int32_t max_context, int32_t head_dim, int waves) {
+                       int32_t max_context, int32_t head_dim, bool q_f32, int waves) {
   DecodePlan p;
   p.waves = waves;
   DecodeArgs& a = p.args;
@@ -201,7 +205,7 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
   }
   const int64_t items32 =
       (int64_t)num_layers * ((num_q_heads + kRowsPerBlock - 1) / kRowsPerBlock) * batch;
-  const int rows = decode_rows(num_q_heads, num_layers, span, items32);
+  const int rows = decode_rows(num_q_heads, num_layers, span, items32, q_f32);
   p.nrt = std::min(rows, (int)num_q_heads) <= 16 ? 1 : 2;
   const int head_blocks = (num_q_heads + rows - 1) / rows;
   if (num_layers * head_blocks > kMaxRowBlocks) {
@@ -290,12 +294,12 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
 // chip measured slower (short ranges are bound by latency, not by the loop).
 DecodePlan plan_decode_auto(int32_t batch, int32_t num_q_heads, int32_t num_layers,
                             const int32_t* layer_slot, const int32_t* layer_window,
-                            int32_t max_context, int32_t head_dim) {
+                            int32_t max_context, int32_t head_dim, bool q_f32) {
   if (tuning().waves)
     return plan_decode(batch, num_q_heads, num_layers, layer_slot, layer_window, max_context,
-                       head_dim, tuning().waves);
+                       head_dim, q_f32, tuning().waves);
   DecodePlan p8 = plan_decode(batch, num_q_heads, num_layers, layer_slot, layer_window,
-                              max_context, head_dim, kDecodeWaves);
+                              max_context, head_dim, q_f32, kDecodeWaves);
   if (p8.rc) return p8;
   const double slots = target_workgroups();
   const double fill8 = p8.args.total_wgs / slots;
@@ -303,7 +307,7 @@ DecodePlan plan_decode_auto(int32_t batch, int32_t num_q_heads, int32_t num_laye
   for (int g = 0; g < p8.args.num_groups; ++g)
     if (p8.args.groups[g].nchunk < 2) return p8;
   DecodePlan p4 = plan_decode(batch, num_q_heads, num_layers, layer_slot, layer_window,
-                              max_context, head_dim, kDecodeWavesSmall);
+                              max_context, head_dim, q_f32, kDecodeWavesSmall);
   if (p4.rc) {
     ok();  // the eight-wavefront plan stands; clear the other's message
     return p8;
@@ -377,14 +381,15 @@ int kv_pack_int8(const void* k, const void* v, mqa_dtype src_dtype, int64_t num_
 
 size_t mqa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_layers,
                                   const int32_t* layer_slot, const int32_t* layer_window,
-                                  int32_t max_context, int32_t head_dim) {
+                                  int32_t max_context, int32_t head_dim, mqa_dtype q_dtype) {
   if (batch <= 0 || num_q_heads <= 0 || num_layers <= 0 || max_context <= 0 || !layer_slot ||
-      !layer_window || (head_dim != 64 && head_dim != 128))
+      !layer_window || (head_dim != 64 && head_dim != 128) ||
+      (q_dtype != MQA_F32 && q_dtype != MQA_BF16))
     return 0;
   for (int l = 0; l < num_layers; ++l)
     if (layer_slot[l] < 0 || layer_window[l] < 0) return 0;
   DecodePlan p = plan_decode_auto(batch, num_q_heads, num_layers, layer_slot, layer_window,
-                                  max_context, head_dim);
+                                  max_context, head_dim, q_dtype == MQA_F32);
   return p.rc ? 0 : p.ws_bytes;
 }
 
@@ -418,7 +423,7 @@ int decode_common(const void* q, mqa_dtype q_dtype, float* out, const void* k_ne
                              layer_window);
   if (rc) return rc;
   DecodePlan p = plan_decode_auto(batch, num_q_heads, num_layers, layer_slot, layer_window,
-                                  max_context, pool->head_dim);
+                                  max_context, pool->head_dim, q_dtype == MQA_F32);
   if (p.rc) return p.rc;
   if (p.ws_bytes > 0) {
     if (!workspace || workspace_bytes < p.ws_bytes)
@@ -541,6 +546,25 @@ int mqa_append_attn(const void* q, mqa_dtype q_dtype, float* out, const mqa_kv_p
   hipError_t e = launch_append(pool->head_dim, q_dtype == MQA_F32, nrt, a, ptrs,
                                static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mqa_append_attn launch");
+  return ok();
+}
+
+}  // extern "C"
+
+extern "C" {
+
+int mqa_hbm_read_probe(const void* src, int64_t bytes, uint32_t* sink, int32_t sink_words,
+                       void* stream) {
+  if (!src || !sink) return fail(MQA_ERR_INVALID, "src and sink must be non-NULL");
+  if (bytes <= 0 || bytes % 16 != 0)
+    return fail(MQA_ERR_INVALID, "bytes = %lld: a positive multiple of 16", (long long)bytes);
+  if (!aligned(src, 16) || !aligned(sink, 4))
+    return fail(MQA_ERR_INVALID, "src must be 16-byte and sink 4-byte aligned");
+  if (sink_words < MQA_PROBE_SINK_WORDS)
+    return fail(MQA_ERR_INVALID, "sink_words %d < %d", sink_words, MQA_PROBE_SINK_WORDS);
+  hipError_t e = launch_hbm_read(src, bytes, sink, MQA_PROBE_SINK_WORDS,
+                                 static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mqa_hbm_read_probe launch");
   return ok();
 }
 

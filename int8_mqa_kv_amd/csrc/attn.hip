@@ -19,17 +19,19 @@
 //    operand is one contiguous 16-byte lane load of a page record
 //    (layout.hpp); decode streams pages HBM -> LDS with gfx950's direct
 //    global -> LDS loads.
-//  * S^T = K.Q^T runs on the int8 matrix cores (16x16x64, exact int32): the K
-//    codes are used as stored, and each q row is scaled by a power of two to
-//    a 15-bit fixed-point integer split into two int8 halves.  O^T += V^T.P^T
-//    runs on fp16 matrix cores (16x16x32, fp32 accumulate) with the V codes
-//    converted exactly to fp16.  The S^T tile a lane receives (4 keys of one
-//    row) is exactly the P^T operand it needs, so the softmax stays in
-//    registers.
+//  * S^T = K.Q^T and O^T += V^T.P^T both run on fp16 matrix cores
+//    (16x16x32, fp32 accumulate).  K and V codes become exact fp16 values
+//    c + 1152 with two byte permutes per four codes; the bias is removed
+//    through the score accumulator's starting value (-1152 * sum of the q
+//    row) and, for PV, through a product of the same P with an all-ones
+//    operand.  q rows are scaled by a power of two into fp16's range, where a
+//    bf16 element is exact (an fp32 element is carried as two fp16 terms).
+//    The S^T tile a lane receives (4 keys of one row) is exactly the P^T
+//    operand it needs, so the softmax stays in registers.
 //  * P*sV is scaled by a power of two tied to the largest V scale seen so
-//    far, so the fp16 P operand keeps full precision.  The remaining
-//    roundings are the fp16 P operand (relative 2^-11), q's fixed point
-//    (elements below 2^-7 of their row's maximum) and fp32 sums.
+//    far and carried as two fp16 terms (hi + lo, within 2^-22 of it), so the
+//    output keeps about 21 bits of every weight.  The remaining roundings are
+//    fp32 sums (the code bias included).
 //  * Online softmax in the log2 domain (v_exp_f32) with a lazily moved
 //    reference maximum per row.
 //  * Decode splits long contexts into chunks (flash-decoding style): the
@@ -83,12 +85,50 @@ __device__ __forceinline__ void zero_page(PageRegs<D>& r) {
 // ---------------------------------------------------------------------------
 // Query operands
 // ---------------------------------------------------------------------------
+// A query row is scaled by 2^(15-E) (E: the exponent of its largest |element|,
+// so the largest scaled element lies in [2^14, 2^15)) and held as fp16
+// matrix-core operands.  A bf16 element keeps all its bits (fp16 has three
+// more, and only elements below 2^-28 of the row's largest fall out of
+// fp16's normal range); an fp32 element is split into two fp16 terms.
 template <int D, int QS, int NRT>
 struct QOps {
-  static constexpr int KS8 = D / 64;  // 16x16x64 int8 steps over the channels
-  u32x4 q8[NRT][2][KS8];               // [row tile][hi, lo][step]: 16 int8 per lane
-  float crow[NRT];  // 2^(E-14) * scale * log2(e): undoes the row's fixed-point scale
+  static constexpr int NQ = QS == 1 ? 1 : 2;  // fp16 terms per element
+  static constexpr int STEPS = D / 32;        // 16x16x32 steps over the channels
+  f16x8 qf[NRT][NQ][STEPS];  // lane (i, g): row 16n+i, channels g*D/4 + 8k .. +7 at step k
+  float bias[NRT];  // -kCodeBias * (sum of the row's fp16 terms): start of every score sum
+  float crow[NRT];  // 2^(E-15) * scale * log2(e): undoes the row's power-of-two scale
 };
+
+// The fp16 terms of PER elements of one query row, already scaled by a power
+// of two, and their sum in fp32 (this lane's share of the bias).
+template <int PER, int NQ>
+__device__ __forceinline__ float q_terms(const float (&x)[PER], float sc, _Float16 (&t)[NQ][PER]) {
+  float sum = 0.0f;
+#pragma unroll
+  for (int e = 0; e < PER; e += 2) {
+    const float y0 = x[e] * sc, y1 = x[e + 1] * sc;
+    if constexpr (NQ == 1) {
+      t[0][e] = (_Float16)y0;
+      t[0][e + 1] = (_Float16)y1;
+      sum += (float)t[0][e] + (float)t[0][e + 1];
+    } else {
+      f16x2 hi, lo;
+      split_f16x2(y0, y1, hi, lo);
+      t[0][e] = hi[0];
+      t[0][e + 1] = hi[1];
+      t[1][e] = lo[0];
+      t[1][e + 1] = lo[1];
+      sum += ((float)hi[0] + (float)lo[0]) + ((float)hi[1] + (float)lo[1]);
+    }
+  }
+  return sum;
+}
+
+// Exponent E of a row's largest |element| a (a in [2^(E-1), 2^E)); 0 for an
+// all-zero row.  E >= -100 keeps 2^(15-E) finite for absurdly small rows.
+__device__ __forceinline__ int q_row_exp(float a) {
+  return a > 0.0f ? max(frexp_exp(a), -100) : 0;
+}
 
 // Raw query registers of one wavefront: rows 16n + li, channels lg*CH .. +CH.
 template <int D, int QS, int NRT>
@@ -115,14 +155,14 @@ __device__ __forceinline__ void load_q_raw(QRaw<D, QS, NRT>& r, const void* __re
   }
 }
 
-// Turn the raw rows into int8 matrix-core operands: scale each row by a power
-// of two so that its largest |element| lies in [2^13, 2^14), round to an
-// integer and split it into two int8 halves (q15_word, q15_pack4).  Lane (i, g) owns
-// row i's channels g*CH .. g*CH+CH-1, exactly its B-operand bytes.
+// Turn the raw rows into fp16 matrix-core operands.  Lane (i, g) owns row i's
+// channels g*CH .. g*CH+CH-1, which are exactly its B-operand elements of the
+// STEPS steps (8 per step, in order).
 template <int D, int QS, int NRT>
 __device__ __forceinline__ void convert_q(QOps<D, QS, NRT>& o, const QRaw<D, QS, NRT>& r,
                                           float scale_log2, int nrows, int li) {
   constexpr int CH = Geo<D>::CH;
+  constexpr int NQ = QOps<D, QS, NRT>::NQ;
 #pragma unroll
   for (int n = 0; n < NRT; ++n) {
     const bool live = 16 * n + li < nrows;
@@ -146,21 +186,17 @@ __device__ __forceinline__ void convert_q(QOps<D, QS, NRT>& o, const QRaw<D, QS,
     float a = 0.0f;
 #pragma unroll
     for (int c = 0; c < CH; ++c) a = fmaxf(a, fabsf(x[c]));
-    a = row_max4(a);
-    const int E = a > 0.0f ? max(frexp_exp(a), -100) : 14;
-    const float sc = ldexp2(1.0f, 14 - E);
-    o.crow[n] = ldexp2(scale_log2, E - 14);
+    const int E = q_row_exp(row_max4(a));
+    _Float16 t[NQ][CH];
+    const float sum = row_sum4(q_terms<CH, NQ>(x, ldexp2(1.0f, 15 - E), t));
+    o.crow[n] = ldexp2(scale_log2, E - 15);
+    o.bias[n] = -kCodeBias * sum;
 #pragma unroll
-    for (int h = 0; h < QOps<D, QS, NRT>::KS8; ++h)
+    for (int p = 0; p < NQ; ++p)
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const float* xs = x + 16 * h + 4 * d;
-        uint32_t hw, lw;
-        q15_pack4(q15_word(xs[0], sc), q15_word(xs[1], sc), q15_word(xs[2], sc),
-                  q15_word(xs[3], sc), hw, lw);
-        o.q8[n][0][h][d] = hw;
-        o.q8[n][1][h][d] = lw;
-      }
+      for (int k = 0; k < QOps<D, QS, NRT>::STEPS; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o.qf[n][p][k][e] = t[p][8 * k + e];
   }
 }
 
@@ -186,7 +222,7 @@ struct WaveState {
     }
     ev = kNoExp;
   }
-  // The accumulators hold P.(V codes + kVBias): remove kVBias * sum(P).
+  // The accumulators hold P.(V codes + kCodeBias): remove kCodeBias * sum(P).
   __device__ __forceinline__ void unbias() {
 #pragma unroll
     for (int n = 0; n < NRT; ++n)
@@ -194,7 +230,7 @@ struct WaveState {
       for (int t = 0; t < Geo<D>::VT; ++t)
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          acc[n][t][k] = __builtin_fmaf(-kVBias, psum[n][k], acc[n][t][k]);
+          acc[n][t][k] = __builtin_fmaf(-kCodeBias, psum[n][k], acc[n][t][k]);
   }
 };
 
@@ -215,24 +251,28 @@ __device__ __forceinline__ void attend_block(WaveState<D, NRT>& st, const QOps<D
                                              const PageRegs<D>& p0, const PageRegs<D>& p1,
                                              bool ok0, bool ok1, int pos0, int lo, int hi,
                                              int lg) {
-  constexpr int KS8 = D / 64;
-  // S^T for both pages on the int8 matrix cores: the K codes are the A operand
-  // as stored (lane (i, g): token i, 16 channels per step); q's two int8
-  // halves are B.  Lane (i, g) gets the scores of keys 4g..4g+3 for row i.
+  constexpr int STEPS = QOps<D, QS, NRT>::STEPS, NQ = QOps<D, QS, NRT>::NQ;
+  // S^T for both pages on the fp16 matrix cores: 8 stored K bytes (token i,
+  // channels g*D/4 + 8k ..) are lane (i, g)'s A operand of step k as fp16
+  // c + kCodeBias; the q row is B.  Each sum starts at -kCodeBias * (the
+  // row's sum), which takes the bias back out.  Lane (i, g) gets the scores
+  // of keys 4g..4g+3 for row i.
   f32x4 s[NRT][2];
 #pragma unroll
   for (int n = 0; n < NRT; ++n)
 #pragma unroll
+    for (int u = 0; u < 2; ++u) s[n][u] = f32x4{q.bias[n], q.bias[n], q.bias[n], q.bias[n]};
+#pragma unroll
+  for (int k = 0; k < STEPS; ++k)
+#pragma unroll
     for (int u = 0; u < 2; ++u) {
       const PageRegs<D>& P = u ? p1 : p0;
-      i32x4 shi = i32x4{0, 0, 0, 0}, slo = i32x4{0, 0, 0, 0};
+      const int h = k >> 1, w = 2 * (k & 1);
+      const f16x8 kop = codes_to_f16x8_biased(P.k[h][w], P.k[h][w + 1]);
 #pragma unroll
-      for (int h = 0; h < KS8; ++h) {
-        shi = mma_i8(P.k[h], q.q8[n][0][h], shi);
-        slo = mma_i8(P.k[h], q.q8[n][1][h], slo);
-      }
+      for (int n = 0; n < NRT; ++n)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s[n][u][r] = (float)((shi[r] << 8) + slo[r]);
+        for (int t = 0; t < NQ; ++t) s[n][u] = mma16(kop, q.qf[n][t][k], s[n][u]);
     }
 
   bool valid[2][4];
@@ -303,38 +343,50 @@ __device__ __forceinline__ void attend_block(WaveState<D, NRT>& st, const QOps<D
     }
   }
 
-  f16x8 pop[NRT];
+  // P*sV as two fp16 terms, hi and lo (hi + lo within 2^-22 of it)
+  f16x8 ph[NRT], pl[NRT];
 #pragma unroll
   for (int n = 0; n < NRT; ++n) {
     float ps = 0.0f;
+    float pv[8];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float pr = fast_exp2(__builtin_fmaf(t[n][u][r], q.crow[n], neg_m[n]));
         ps += pr;
-        const float pv = pr * ((u ? p1.sv : p0.sv)[r] * pvm);
-        pop[n][4 * u + r] = (_Float16)(MASKED ? (valid[u][r] ? pv : 0.0f) : pv);
+        const float x = pr * ((u ? p1.sv : p0.sv)[r] * pvm);
+        pv[4 * u + r] = MASKED ? (valid[u][r] ? x : 0.0f) : x;
       }
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      f16x2 hi, lo;
+      split_f16x2(pv[e], pv[e + 1], hi, lo);
+      ph[n][e] = hi[0];
+      ph[n][e + 1] = hi[1];
+      pl[n][e] = lo[0];
+      pl[n][e + 1] = lo[1];
+    }
     st.l[n] = st.l[n] * alpha[n] + ps;
   }
-  // V codes enter as c + kVBias (two byte permutes per four codes); the
-  // matching sum of P comes from one more product with an all-ones operand,
-  // so it uses the very fp16 P values the accumulators saw.
+  // V codes enter as c + kCodeBias (two byte permutes per four codes); the
+  // matching sum of P comes from products with an all-ones operand, so it
+  // uses the very fp16 terms the accumulators saw.
 #pragma unroll
   for (int t = 0; t < Geo<D>::VT; ++t) {
     const int h = t >> 2, dw = t & 3;
-    f16x2 a0, a1, b0, b1;
-    v_bytes_to_f16x4_biased(p0.v[h][dw], a0, a1);
-    v_bytes_to_f16x4_biased(p1.v[h][dw], b0, b1);
-    const f16x8 vop = {a0[0], a0[1], a1[0], a1[1], b0[0], b0[1], b1[0], b1[1]};
+    const f16x8 vop = codes_to_f16x8_biased(p0.v[h][dw], p1.v[h][dw]);
 #pragma unroll
-    for (int n = 0; n < NRT; ++n) st.acc[n][t] = mma16(vop, pop[n], st.acc[n][t]);
+    for (int n = 0; n < NRT; ++n) st.acc[n][t] = mma16(vop, ph[n], st.acc[n][t]);
+#pragma unroll
+    for (int n = 0; n < NRT; ++n) st.acc[n][t] = mma16(vop, pl[n], st.acc[n][t]);
   }
   const _Float16 one = 1.0f;
   const f16x8 ones = {one, one, one, one, one, one, one, one};
 #pragma unroll
-  for (int n = 0; n < NRT; ++n) st.psum[n] = mma16(ones, pop[n], st.psum[n]);
+  for (int n = 0; n < NRT; ++n) st.psum[n] = mma16(ones, ph[n], st.psum[n]);
+#pragma unroll
+  for (int n = 0; n < NRT; ++n) st.psum[n] = mma16(ones, pl[n], st.psum[n]);
 }
 
 template <int D, int QS, int NRT>
@@ -530,9 +582,9 @@ __device__ __forceinline__ void lds_page(PageRegs<D>& r, const uint8_t* lds_slot
 // loads) so that the compiler can tell them apart.
 template <int D, int QS, int NRT, int W>
 struct DecodeQLds {
-  static constexpr int KS8 = D / 64;
-  u32x4 q8[NRT][2][KS8][64];
+  f16x8 qf[NRT][QOps<D, QS, NRT>::NQ][QOps<D, QS, NRT>::STEPS][64];
   float crow[32];
+  float qb[32];
   float m[W][32];
   float l[W][32];
   int ev[W];
@@ -562,7 +614,7 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// The block's query rows staged into int8 matrix-core operands in LDS, once
+// The block's query rows staged into fp16 matrix-core operands in LDS, once
 // for all W wavefronts: wavefront w takes rows 4w..4w+3, 4w+4W.., 16 lanes per
 // row, D/16 channels per lane.  The raw rows travel global -> LDS first
 // (StageQ::issue, into the wavefront's own staging area): such loads are
@@ -610,6 +662,7 @@ struct StageQ {
   __device__ __forceinline__ void store(Lds& sm, const uint8_t* stage, int nrows,
                                         float scale_log2, int wv, int lane) const {
     constexpr int CH = Geo<D>::CH;
+    constexpr int NQ = QOps<D, QS, NRT>::NQ;
     const int sub = lane >> 4, part = lane & 15;
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
@@ -640,29 +693,30 @@ struct StageQ {
       }
 #pragma unroll
       for (int off = 1; off < 16; off <<= 1) a = fmaxf(a, __shfl_xor(a, off));
-      const int E = a > 0.0f ? max(frexp_exp(a), -100) : 14;
-      const float sc = ldexp2(1.0f, 14 - E);
-      if (part == 0) sm.crow[row] = ldexp2(scale_log2, E - 14);
-      // operand bytes of (row, channels c0..c0+PER-1): tile n, lane (li, lg),
-      // step h, byte offset e0 inside the lane's 16 bytes
+      const int E = q_row_exp(a);
+      _Float16 t[NQ][PER];
+      float sum = q_terms<PER, NQ>(x, ldexp2(1.0f, 15 - E), t);
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) sum += __shfl_xor(sum, off);
+      if (part == 0) {
+        sm.crow[row] = ldexp2(scale_log2, E - 15);
+        sm.qb[row] = -kCodeBias * sum;
+      }
+      // operand elements of (row, channels c0..c0+PER-1): tile n, lane (li,
+      // lg), step k, element e0 of the lane's eight
       const int c0 = part * PER;
       const int n = row >> 4, li = row & 15;
-      const int lg = c0 / CH, h = (c0 % CH) >> 4, e0 = c0 & 15;
-      uint32_t hw[PER / 4], lw[PER / 4];
+      const int lg = c0 / CH, k = (c0 % CH) >> 3, e0 = c0 & 7;
 #pragma unroll
-      for (int d = 0; d < PER / 4; ++d)
-        q15_pack4(q15_word(x[4 * d], sc), q15_word(x[4 * d + 1], sc), q15_word(x[4 * d + 2], sc),
-                  q15_word(x[4 * d + 3], sc), hw[d], lw[d]);
-      uint32_t* dh = reinterpret_cast<uint32_t*>(&sm.q8[n][0][h][16 * lg + li]) + e0 / 4;
-      uint32_t* dl = reinterpret_cast<uint32_t*>(&sm.q8[n][1][h][16 * lg + li]) + e0 / 4;
-      if constexpr (PER == 8) {
-        *reinterpret_cast<u32x2*>(dh) = u32x2{hw[0], hw[1]};
-        *reinterpret_cast<u32x2*>(dl) = u32x2{lw[0], lw[1]};
-      } else {
-#pragma unroll
-        for (int d = 0; d < PER / 4; ++d) {
-          dh[d] = hw[d];
-          dl[d] = lw[d];
+      for (int p = 0; p < NQ; ++p) {
+        _Float16* dst = reinterpret_cast<_Float16*>(&sm.qf[n][p][k][16 * lg + li]) + e0;
+        if constexpr (PER == 8) {
+          *reinterpret_cast<f16x8*>(dst) =
+              f16x8{t[p][0], t[p][1], t[p][2], t[p][3], t[p][4], t[p][5], t[p][6], t[p][7]};
+        } else {
+          static_assert(PER == 4, "channels per lane");
+          *reinterpret_cast<f16x2*>(dst) = f16x2{t[p][0], t[p][1]};
+          *reinterpret_cast<f16x2*>(dst + 2) = f16x2{t[p][2], t[p][3]};
         }
       }
     }
@@ -711,8 +765,8 @@ struct CurrentToken {
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
       const int c = lane * PER + e;
-      rec[k_code_offset(D, j, c)] = (uint8_t)ck[e];
-      rec[v_code_offset(D, j, c)] = v_code_byte(cv[e]);
+      rec[k_code_offset(D, j, c)] = code_byte(ck[e]);
+      rec[v_code_offset(D, j, c)] = code_byte(cv[e]);
     }
     if (lane == 0) {
       *reinterpret_cast<float*>(rec + k_scale_offset(D, j)) = sk;
@@ -874,10 +928,11 @@ __global__ __launch_bounds__(W * 64, 2) void decode_kernel(
 #pragma unroll
   for (int n = 0; n < NRT; ++n) {
     q.crow[n] = sm.crow[16 * n + li];
+    q.bias[n] = sm.qb[16 * n + li];
 #pragma unroll
-    for (int hl = 0; hl < 2; ++hl)
+    for (int p = 0; p < QOps<D, QS, NRT>::NQ; ++p)
 #pragma unroll
-      for (int h = 0; h < D / 64; ++h) q.q8[n][hl][h] = sm.q8[n][hl][h][lane];
+      for (int k = 0; k < QOps<D, QS, NRT>::STEPS; ++k) q.qf[n][p][k] = sm.qf[n][p][k][lane];
   }
 
   WaveState<D, NRT> st;
@@ -1274,12 +1329,14 @@ static hipError_t launch_decode_n(int waves, NewKV nk, const DecodeArgs& a, cons
 hipError_t launch_decode(int D, bool q_f32, int nrt, int waves, NewKV nk, const DecodeArgs& a,
                          const DecodePtrs& p, hipStream_t stream) {
 #define MQA_DEC(DD, QQ, NN) return launch_decode_n<DD, QQ, NN>(waves, nk, a, p, stream)
+  // fp32 queries run one 16-row tile per wavefront (the planner's rows)
+  if (q_f32 && nrt != 1) return hipErrorInvalidValue;
   if (D == 128) {
-    if (q_f32) { if (nrt == 1) MQA_DEC(128, 2, 1); MQA_DEC(128, 2, 2); }
+    if (q_f32) MQA_DEC(128, 2, 1);
     if (nrt == 1) MQA_DEC(128, 1, 1);
     MQA_DEC(128, 1, 2);
   }
-  if (q_f32) { if (nrt == 1) MQA_DEC(64, 2, 1); MQA_DEC(64, 2, 2); }
+  if (q_f32) MQA_DEC(64, 2, 1);
   if (nrt == 1) MQA_DEC(64, 1, 1);
   MQA_DEC(64, 1, 2);
 #undef MQA_DEC

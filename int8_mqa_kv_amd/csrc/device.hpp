@@ -1,5 +1,6 @@
 // Device helpers shared by the gfx950 kernels: vector types, exact int8 ->
-// fp16 conversion, matrix-core wrapper, wavefront reductions.
+// fp16 conversion, two-term fp16 splits, matrix-core wrapper, wavefront
+// reductions.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -26,18 +27,27 @@ __device__ __forceinline__ T bitcast(F f) {
   return __builtin_bit_cast(T, f);
 }
 
-// Four stored V bytes (one dword, byte k = code k + 128) -> four exact fp16
-// values c + kVBias.  Each byte goes under the fp16 exponent of 1024 (bits
+// Four stored code bytes (one dword, byte k = code k + 128: K and V codes
+// are both stored with the sign bit flipped) -> four exact fp16 values
+// c + kCodeBias.  Each byte goes under the fp16 exponent of 1024 (bits
 // 0x64uu = 1024 + u, exact for u < 1024) with one byte permute per pair, so
-// the value is 1024 + 128 + c = 1152 + c.  A product of these with P carries
-// kVBias * sum(P), which the caller removes once, from the same P summed on
-// the matrix cores.
-constexpr float kVBias = 1152.0f;
-__device__ __forceinline__ void v_bytes_to_f16x4_biased(uint32_t u, f16x2& lo, f16x2& hi) {
+// the value is 1024 + 128 + c = 1152 + c.  A product of these with another
+// operand carries kCodeBias times that operand's sum, which the caller
+// removes: for Q.K^T through the accumulator's starting value, for P.V from
+// a product of the same P with an all-ones operand.
+constexpr float kCodeBias = 1152.0f;
+__device__ __forceinline__ void codes_to_f16x4_biased(uint32_t u, f16x2& lo, f16x2& hi) {
   // v_perm_b32: selector bytes 0-3 pick bytes of the second operand, 4-7 of
   // the first.  Result bytes (low to high): u.b0, 0x64, u.b1, 0x64.
   lo = bitcast<f16x2>(__builtin_amdgcn_perm(0x64646464u, u, 0x04010400u));
   hi = bitcast<f16x2>(__builtin_amdgcn_perm(0x64646464u, u, 0x04030402u));
+}
+// Eight stored code bytes (two dwords) -> one fp16 matrix-core operand.
+__device__ __forceinline__ f16x8 codes_to_f16x8_biased(uint32_t w0, uint32_t w1) {
+  f16x2 a0, a1, b0, b1;
+  codes_to_f16x4_biased(w0, a0, a1);
+  codes_to_f16x4_biased(w1, b0, b1);
+  return f16x8{a0[0], a0[1], a1[0], a1[1], b0[0], b0[1], b1[0], b1[1]};
 }
 
 // D = A.B + C on one 16x16x32 fp16 tile, fp32 accumulate.  Lane l
@@ -47,30 +57,27 @@ __device__ __forceinline__ f32x4 mma16(const f16x8& a, const f16x8& b, const f32
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// D = A.B + C on one 16x16x64 int8 tile, int32 accumulate (exact).  Lane l
-// (i = l % 16, g = l / 16) supplies A[i][16g..16g+15] and B[16g..16g+15][i]
-// (16 bytes each) and receives D[4g..4g+3][i].
-__device__ __forceinline__ i32x4 mma_i8(const u32x4& a, const u32x4& b, const i32x4& c) {
-  return __builtin_amdgcn_mfma_i32_16x16x64_i8(bitcast<i32x4>(a), bitcast<i32x4>(b), c, 0, 0, 0);
+// x - h for an fp32 value x and an fp16 value h held in the low (HI = false)
+// or high (HI = true) half of a packed register, in one mixed-precision FMA
+// (fp32 result, one rounding; exact when h is x rounded to fp16).
+template <bool HI>
+__device__ __forceinline__ float sub_f16_from(float x, f16x2 h) {
+  float r;
+  if constexpr (HI)
+    asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "=v"(r) : "v"(h), "v"(x));
+  else
+    asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x));
+  return r;
 }
 
-// A query element as a 15-bit fixed-point integer v = rint(x * sc)
-// (|x * sc| < 2^14) split into two int8 halves v = 256*hi + lo with
-// hi = floor((v + 128) / 256) in [-64, 64] and lo = v - 256*hi in [-128, 127].
-// fma(x, sc, 1.5*2^23 + 128) lands on the fp32 grid of spacing 1 (the FMA
-// rounds half to even, as rint does), so the low 16 bits of its bits hold
-// t = v + 128 in two's complement: byte 1 of t is hi, byte 0 xor 0x80 is lo.
-__device__ __forceinline__ uint32_t q15_word(float x, float sc) {
-  return bitcast<uint32_t>(__builtin_fmaf(x, sc, 12583040.0f));  // 1.5*2^23 + 128
-}
-// hi and lo int8 halves of four q15_words, packed (element k = byte k)
-__device__ __forceinline__ void q15_pack4(uint32_t t0, uint32_t t1, uint32_t t2, uint32_t t3,
-                                          uint32_t& hi, uint32_t& lo) {
-  // v_perm_b32 selector bytes 0-3 pick the second operand's bytes, 4-7 the first's
-  const uint32_t a = __builtin_amdgcn_perm(t1, t0, 0x05010400u);  // t0.b0 t1.b0 t0.b1 t1.b1
-  const uint32_t b = __builtin_amdgcn_perm(t3, t2, 0x05010400u);  // t2.b0 t3.b0 t2.b1 t3.b1
-  lo = __builtin_amdgcn_perm(b, a, 0x05040100u) ^ 0x80808080u;
-  hi = __builtin_amdgcn_perm(b, a, 0x07060302u);
+// Two fp32 values as a two-term fp16 pair each: hi = fp16(x) and
+// lo = fp16(x - hi).  |x - hi| <= 2^-11 |x| and lo rounds that rest once
+// more, so |hi + lo - x| <= 2^-22 |x| + 2^-25 (the last term: a rest below
+// fp16's normal range is kept to fp16's subnormal spacing).
+__device__ __forceinline__ void split_f16x2(float x0, float x1, f16x2& hi, f16x2& lo) {
+  hi = f16x2{(_Float16)x0, (_Float16)x1};
+  lo = f16x2{(_Float16)sub_f16_from<false>(x0, hi), (_Float16)sub_f16_from<true>(x1, hi)};
 }
 
 // Reductions across the four lanes i, i+16, i+32, i+48 (one matrix row) with

@@ -121,6 +121,11 @@ hipError_t launch_decode(int D, bool q_f32, int nrt, int waves, NewKV new_kv, co
 hipError_t launch_append(int D, bool q_f32, int nrt, const AppendArgs& a, const AppendPtrs& p,
                          hipStream_t stream);
 
+// Streaming read of `bytes` (a multiple of 16) by `groups` workgroups, each
+// writing the XOR of its range's 32-bit words to sink[its index].
+hipError_t launch_hbm_read(const void* src, int64_t bytes, uint32_t* sink, int groups,
+                           hipStream_t stream);
+
 // Decode workspace: a fixed prefix of 32-bit arrival counters, one per
 // (row block, sequence, wavefront) of a call and each on a 128-byte line of
 // its own (atomics to one line serialise), then one partial record per

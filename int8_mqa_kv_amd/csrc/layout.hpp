@@ -13,8 +13,9 @@
 // matrix-core instructions: lane l (i = l % 16, g = l / 16) of a wavefront
 // reads 16 contiguous bytes at offset 16*l (+1024 for the second half at
 // D = 128), and those bytes are exactly that lane's operand:
-//   K block: lane (i, g) gets token i, channels g*D/4 .. g*D/4 + D/4 - 1
-//            (the QK^T operand: keys are the M index, channels the K index);
+//   K block: lane (i, g) gets token i, channels g*D/4 + 16h .. g*D/4 + 16h + 15
+//            in 1 KiB piece h (the QK^T operand: keys are the M index,
+//            channels the K index; 8 bytes make one 16x16x32 step);
 //   V block: lane (i, g) gets, for 4 channel tiles t, channel 16t + i of the
 //            tokens 4g .. 4g+3 (the PV operand: channels are the M index,
 //            keys the K index).
@@ -22,10 +23,10 @@
 // reads 1 KiB of consecutive bytes per instruction) and needs no LDS
 // transpose.
 //
-// K codes are stored as two's-complement int8.  V codes are stored with the
-// sign bit flipped (byte = code xor 0x80 = code + 128, an unsigned byte): the
-// fp16 operand conversion places that byte under a fixed exponent as it is,
-// with no per-dword fix-up in the attention loop.
+// K and V codes are both stored with the sign bit flipped (byte = code xor
+// 0x80 = code + 128, an unsigned byte): the fp16 operand conversion places
+// that byte under a fixed exponent as it is, with no per-dword fix-up in the
+// attention loop.
 #pragma once
 #include <stdint.h>
 
@@ -55,8 +56,8 @@ MQA_HD constexpr int v_code_offset(int D, int j, int c) {
          ((c >> 4) & 3) * 4 + (j & 3);
 }
 
-// Stored byte of V code c (-127..127): c + 128.
-MQA_HD constexpr uint8_t v_code_byte(int c) { return (uint8_t)(c ^ 0x80); }
+// Stored byte of a K or V code c (-127..127): c + 128.
+MQA_HD constexpr uint8_t code_byte(int c) { return (uint8_t)(c ^ 0x80); }
 
 MQA_HD constexpr int k_scale_offset(int D, int j) { return 32 * D + 4 * j; }
 MQA_HD constexpr int v_scale_offset(int D, int j) { return 32 * D + 64 + 4 * j; }

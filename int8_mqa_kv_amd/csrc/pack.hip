@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kPackWaves * 64) void pack_kernel(
       const int c = lane * PER + e;
       const int off = which == 0 ? k_code_offset(D, j, c) : v_code_offset(D, j, c);
       const int code = quant_code(x[e], a, s);
-      rec[off] = which == 0 ? (uint8_t)(int8_t)code : v_code_byte(code);
+      rec[off] = code_byte(code);
     }
     if (lane == 0) {
       const int off = which == 0 ? k_scale_offset(D, j) : v_scale_offset(D, j);

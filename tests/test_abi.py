@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_sizes():
-    assert mk.lib.mqa_abi_version() == 4
+    assert mk.lib.mqa_abi_version() == 5
     assert mk.page_bytes(128) == 32 * 128 + 128 == 4224
     assert mk.page_bytes(64) == 2176
     assert mk.lib.mqa_page_bytes(96) == 0
@@ -110,7 +110,12 @@ def test_decode_workspace_sizes():
     # d = 128, at least two records per sequence)
     assert ws2 % 256 == 0
     assert ws2 >= (8 << 20) + 16 * 2 * 16 * 288 * 4
-    assert mk.lib.mqa_decode_workspace_bytes(0, 32, 1, None, None, 4096, 128) == 0
+    assert mk.lib.mqa_decode_workspace_bytes(0, 32, 1, None, None, 4096, 128, mk.MQA_BF16) == 0
+    # fp32 queries take 16-row blocks: twice the items, half the chunks each
+    # here (the same 256 partial records)
+    assert mk.decode_workspace_bytes(16, 32, [0], [0], 32768, 128, 'f32') == ws2
+    with pytest.raises(ValueError):
+        mk.decode_workspace_bytes(16, 32, [0], [0], 32768, 128, 'f16')
     assert ws1 >= 0
 
 
@@ -178,8 +183,8 @@ def test_unpack_roundtrip_on_host():
     ks = g.random(16).astype(np.float32)
     vs = g.random(16).astype(np.float32)
     page = np.zeros(mk.page_bytes(d), np.uint8)
-    page[k_off] = kc.view(np.uint8)
-    page[v_off] = (vc.astype(np.int16) + 128).astype(np.uint8)  # V codes stored as c + 128
+    page[k_off] = (kc.astype(np.int16) + 128).astype(np.uint8)  # codes stored as c + 128
+    page[v_off] = (vc.astype(np.int16) + 128).astype(np.uint8)
     for j in range(16):
         page[ks_off[j]:ks_off[j] + 4] = np.frombuffer(ks[j].tobytes(), np.uint8)
         page[vs_off[j]:vs_off[j] + 4] = np.frombuffer(vs[j].tobytes(), np.uint8)
@@ -187,3 +192,17 @@ def test_unpack_roundtrip_on_host():
     a, b, c, e = mk.unpack_page_tokens(pool, 16 + np.arange(16), d)
     assert np.array_equal(a, kc) and np.array_equal(b, ks)
     assert np.array_equal(c, vc) and np.array_equal(e, vs)
+
+
+def test_probe_rejects_bad_arguments():
+    """Host-side checks of mqa_hbm_read_probe run before any launch."""
+    rc = mk.lib.mqa_hbm_read_probe(0x1000, 24, 0x2000, mk.PROBE_SINK_WORDS, None)
+    assert rc == mk.MQA_ERR_INVALID and "multiple of 16" in mk.lib.mqa_last_error().decode()
+    rc = mk.lib.mqa_hbm_read_probe(0x1000, 0, 0x2000, mk.PROBE_SINK_WORDS, None)
+    assert rc == mk.MQA_ERR_INVALID
+    rc = mk.lib.mqa_hbm_read_probe(0x1000, 4096, 0x2000, mk.PROBE_SINK_WORDS - 1, None)
+    assert rc == mk.MQA_ERR_INVALID and "sink_words" in mk.lib.mqa_last_error().decode()
+    rc = mk.lib.mqa_hbm_read_probe(0x1008, 4096, 0x2000, mk.PROBE_SINK_WORDS, None)
+    assert rc == mk.MQA_ERR_INVALID and "aligned" in mk.lib.mqa_last_error().decode()
+    rc = mk.lib.mqa_hbm_read_probe(None, 4096, 0x2000, mk.PROBE_SINK_WORDS, None)
+    assert rc == mk.MQA_ERR_INVALID

@@ -1,11 +1,14 @@
 """mqa_append_attn on the GPU against the oracle."""
+import time
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import synth
-from tests.gpu_util import GpuCase, OracleKV, assert_parity, assert_parity_peaked, log, q_tensor
+from tests.gpu_util import (MAX_ABS, REL_L2, GpuCase, OracleKV, assert_parity, log, outlier_q,
+                            q_tensor)
 
 pytestmark = pytest.mark.gpu
 
@@ -50,23 +53,51 @@ def test_append_one_token_matches_decode():
     q, q64 = q_tensor(w)
     app = g.append(q).cpu().numpy()
     dec = g.decode(q).cpu().numpy()          # [L, total_q = B, Hq, D] is decode's layout
-    # The two kernels split the keys differently, so the fp16 P operand is
-    # rounded against different running maxima: each side is within 2^-12 of
-    # |out| of the exact result (both are checked against the oracle elsewhere).
-    np.testing.assert_allclose(app, dec, rtol=0, atol=1e-3)
+    # The two kernels split the keys differently: the same terms summed in
+    # another order and against other running maxima.
+    diff = float(np.abs(app - dec).max())
+    log(f"  append q_len=1 vs decode: max |diff| {diff:.2e}")
+    assert diff <= 1e-4
     want = oracle.decode(q64, w.context_lens, w.layer_slot, w.layer_window, OracleKV(w))
     assert_parity(app, want, "append q_len=1")
     assert_parity(dec, want, "decode of the same rows")
 
 
-def test_case4_hybrid_turn_sampled():
-    """The full hybrid turn (256 sequences, 12 layers) on the GPU; the oracle
-    checks every output of a sample of sequences (shortest, longest, median
-    and a few random ones)."""
+@pytest.mark.timeout(1200)
+def test_case4_hybrid_turn_full():
+    """The full hybrid turn (256 sequences x 64 appended tokens, 12 layers, 11
+    slots) on the GPU against the oracle on every output row: about 6.6e12
+    fp64 flop on the host cores, taken 16 sequences at a time (each a
+    sub-problem of its own) with the maximum error and the L2 sums gathered
+    over the whole output."""
     w = synth.case4()
-    order = np.argsort(w.context_lens)
-    seqs = sorted(set([int(order[0]), int(order[-1]), int(order[len(order) // 2]), 7, 101, 200]))
-    _run(w, seqs=seqs)
+    log(f"append case 4: B={w.batch} L={w.num_layers} total_q={int(w.cu_q_lens[-1])}")
+    g = GpuCase(w)
+    q, q64 = q_tensor(w)
+    got_all = g.append(q).cpu().numpy()
+    kv = OracleKV(w)
+    cu, ctx = w.cu_q_lens.astype(np.int64), w.context_lens.astype(np.int64)
+    max_abs, sq_diff, sq_ref, t0 = 0.0, 0.0, 0.0, time.time()
+    for c0 in range(0, w.batch, 16):
+        seqs = list(range(c0, min(w.batch, c0 + 16)))
+        rows = np.concatenate([np.arange(cu[b], cu[b + 1]) for b in seqs])
+        cu_sub = np.concatenate([[0], np.cumsum([cu[b + 1] - cu[b] for b in seqs])])
+        want = oracle.append(q64[:, rows], ctx[seqs], cu_sub, w.layer_slot, w.layer_window,
+                             lambda s_, i: kv(s_, seqs[i]))
+        got = got_all[:, rows].astype(np.float64)
+        assert np.all(np.isfinite(got)), f"sequences {seqs[0]}..{seqs[-1]}: non-finite output"
+        d = got - want
+        max_abs = max(max_abs, float(np.abs(d).max()))
+        sq_diff += float(np.sum(d * d))
+        sq_ref += float(np.sum(want * want))
+        for b in seqs:
+            for s_ in range(w.num_slots):
+                kv.cache.pop((s_, b), None)
+        log(f"  sequences {seqs[0]}..{seqs[-1]}: max_abs so far {max_abs:.3e} "
+            f"({time.time() - t0:.0f} s)")
+    rel = (sq_diff / sq_ref) ** 0.5
+    log(f"  parity append case 4 (whole output): max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    assert max_abs <= MAX_ABS and rel <= REL_L2
 
 
 def test_append_peaked_softmax():
@@ -78,4 +109,17 @@ def test_append_peaked_softmax():
     out = g.append(q)
     want = oracle.append(q64, w.context_lens, w.cu_q_lens, w.layer_slot, w.layer_window,
                          OracleKV(w))
-    assert_parity_peaked(out.cpu().numpy(), want, w, "append, peaked softmax")
+    assert_parity(out.cpu().numpy(), want, "append, peaked softmax")
+
+
+@pytest.mark.parametrize("gain", [64, 512])
+def test_append_outlier_query_channels(gain):
+    """Append rows whose four outlier q channels are 64 or 512 times the rest."""
+    w = synth.custom_append(48, [900, 3000], [64, 17], 32, 128, [1024, 0], [0, 1])
+    g = GpuCase(w)
+    q, q64 = q_tensor(w)
+    q, q64 = outlier_q(q, q64, gain, 700 + gain)
+    out = g.append(q)
+    want = oracle.append(q64, w.context_lens, w.cu_q_lens, w.layer_slot, w.layer_window,
+                         OracleKV(w))
+    assert_parity(out.cpu().numpy(), want, f"append, outlier q x{gain}")

@@ -10,7 +10,7 @@ import torch
 import int8_mqa_kv_amd as mk
 import oracle
 import synth
-from tests.gpu_util import GpuCase, OracleKV, assert_parity, assert_parity_peaked, log, q_tensor
+from tests.gpu_util import GpuCase, OracleKV, assert_parity, log, outlier_q, q_tensor
 
 pytestmark = pytest.mark.gpu
 
@@ -132,10 +132,12 @@ def test_shared_launch_equals_separate_launches():
     for li in range(3):
         alone = g.decode(q[li:li + 1].contiguous(), [0], [0]).cpu().numpy()
         assert_parity(alone, want[li:li + 1], f"layer {li} alone")
-        # the two launches split the keys into different chunks, so the fp16
-        # P operand is rounded against different running maxima (each within
-        # 2^-12 of |out| of the exact result)
-        np.testing.assert_allclose(together[li], alone[0], rtol=0, atol=1e-3)
+        # the two launches split the keys into different chunks: the same
+        # terms summed in another order and against other running maxima
+        # (P is carried to 2^-22, the fp32 sums hold the code bias 1152)
+        diff = float(np.abs(together[li] - alone[0]).max())
+        log(f"  layer {li}: shared launch vs alone max |diff| {diff:.2e}")
+        assert diff <= 1e-4
 
 
 def test_output_only_written_where_expected():
@@ -185,7 +187,8 @@ def test_loose_host_context_bound(windows):
                                                 w.poison_page, np.int32)], axis=2)
     bound = bt.shape[2] * 16
     bt_t = torch.from_numpy(np.ascontiguousarray(bt)).cuda()
-    ws = mk.decode_workspace(w.batch, w.num_q_heads, ls, windows, bound, w.head_dim)
+    ws = mk.decode_workspace(w.batch, w.num_q_heads, ls, windows, bound, w.head_dim,
+                             q_dtype=w.q_dtype)
     out = torch.full(tuple(q.shape), float("nan"), dtype=torch.float32, device="cuda")
     mk.mqa_decode_attn(q, out, g.pool, bt_t, g.context_lens, bound, ls, windows, workspace=ws)
     torch.cuda.synchronize()
@@ -206,8 +209,9 @@ def test_many_ragged_sequences(window):
 @pytest.mark.parametrize("window", [0, 1024], ids=["global", "window1024"])
 def test_peaked_softmax(window):
     """q scaled by 16 (exact in bf16): every row's weights concentrate on a
-    few keys, where the fp16 P operand's rounding shows most, and the running
-    maximum moves in large steps."""
+    few keys, so the output sits near single V rows (up to |V| ~ 4.6) and any
+    relative rounding of a weight shows in full; the running maximum moves in
+    large steps."""
     w = synth.custom_decode(30 + (window > 0), 4, 32, 128, "bf16", [300, 1500, 4096, 9000], 1,
                             window, 2000)
     g = GpuCase(w)
@@ -215,4 +219,21 @@ def test_peaked_softmax(window):
     q, q64 = q * 16, q64 * 16
     out = g.decode(q)
     want = oracle.decode(q64, w.context_lens, w.layer_slot, w.layer_window, OracleKV(w))
-    assert_parity_peaked(out.cpu().numpy(), want, w, f"peaked softmax, window {window}")
+    assert_parity(out.cpu().numpy(), want, f"peaked softmax, window {window}")
+
+
+@pytest.mark.parametrize("gain", [64, 512])
+@pytest.mark.parametrize("window", [0, 1024], ids=["global", "window1024"])
+def test_outlier_query_channels(gain, window):
+    """bf16 q rows whose four outlier channels are 64 or 512 times the rest:
+    a row's power-of-two scale is set by its outliers, so its ordinary
+    elements sit far below its largest.  fp16 still holds every bf16 element
+    of such a row exactly."""
+    w = synth.custom_decode(60 + (window > 0), 4, 32, 128, "bf16", [300, 1500, 4096, 9000], 1,
+                            window, 2000)
+    g = GpuCase(w)
+    q, q64 = q_tensor(w)
+    q, q64 = outlier_q(q, q64, gain, 600 + gain)
+    out = g.decode(q)
+    want = oracle.decode(q64, w.context_lens, w.layer_slot, w.layer_window, OracleKV(w))
+    assert_parity(out.cpu().numpy(), want, f"outlier q x{gain}, window {window}")

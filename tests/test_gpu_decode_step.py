@@ -88,7 +88,8 @@ def check_step(w, layer_slot=None, layer_window=None, kv_dtype=torch.float32):
 
     g = GpuCase(w)
     garble_positions(g, w, w.context_lens.astype(np.int64) - 1, sorted(set(ls)))
-    ws = mk.decode_workspace(w.batch, w.num_q_heads, ls, lw, w.max_context, w.head_dim)
+    ws = mk.decode_workspace(w.batch, w.num_q_heads, ls, lw, w.max_context, w.head_dim,
+                             q_dtype=w.q_dtype)
     out = run_step(g, q, k_new, v_new, g.context_lens, w.max_context, ls, lw, ws)
     assert torch.equal(g.pool.data, ref.pool.data), "pool bytes differ from kv_pack_int8's"
     assert torch.equal(out, want_out), "output differs from kv_pack_int8 + mqa_decode_attn"
@@ -148,7 +149,8 @@ def test_two_steps_in_a_row():
     ctx = w.context_lens.astype(np.int64)
     garble_positions(g, w, ctx - 2, sorted(set(ls)))
     garble_positions(g, w, ctx - 1, sorted(set(ls)))
-    ws = mk.decode_workspace(w.batch, w.num_q_heads, ls, lw, w.max_context, w.head_dim)
+    ws = mk.decode_workspace(w.batch, w.num_q_heads, ls, lw, w.max_context, w.head_dim,
+                             q_dtype=w.q_dtype)
     okv = OracleKV(w)
     for c in (ctx - 1, ctx):
         k_new, v_new = current_rows(w, c)

@@ -59,7 +59,7 @@ def test_decode_steps_on_recycled_pages():
     torch.cuda.synchronize()
 
     q, q64 = q_tensor(w)
-    ws = mk.decode_workspace(batch, HQ, layer_slot, layer_window, max(final), D)
+    ws = mk.decode_workspace(batch, HQ, layer_slot, layer_window, max(final), D, q_dtype=w.q_dtype)
     cache = {}
 
     def kv_source(slot, seq):
