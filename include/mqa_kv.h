@@ -502,6 +502,34 @@ int mqa_prefix_cache_read_host(const mqa_prefix_cache* cache, const int32_t* tok
                                int64_t pages, uint8_t* out, uint64_t* present);
 
 /*
+ * mqa_decode_step_noalloc -- mqa_decode_step for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same computation, outputs and
+ * stored bytes as mqa_decode_step, with no workspace argument.  Its scratch
+ * (arrival counters and partial softmax records) is a static device array of
+ * the library of MQA_DECODE_STATIC_SCRATCH_BYTES, one copy per GPU, held
+ * until the process ends; the call allocates nothing and calls no
+ * hipMalloc/hipFree.  The first call on a device looks up that device's copy
+ * (with the device current) and clears its counters with a small kernel on
+ * `stream`.  Every call on one GPU shares that GPU's copy, which keeps the
+ * last call's contents: calls that overlap on one GPU (other streams,
+ * other host threads) race and give undefined results; calls on one stream
+ * never overlap.  A launch whose plan needs more scratch than the array
+ * holds (mqa_decode_workspace_bytes of the same arguments, fp32 or bf16 q)
+ * returns MQA_ERR_WORKSPACE before anything is enqueued.  Other arguments
+ * and errors: those of mqa_decode_step.
+ */
+#define MQA_DECODE_STATIC_SCRATCH_BYTES (40u << 20)
+int mqa_decode_step_noalloc(const void* q, mqa_dtype q_dtype, float* out,
+                            const void* k_new, const void* v_new, mqa_dtype kv_dtype,
+                            const mqa_kv_pool* pool, const int32_t* block_table,
+                            int32_t max_pages_per_seq, const int32_t* context_lens,
+                            int32_t max_context, int32_t batch, int32_t num_q_heads,
+                            int32_t num_layers, int32_t num_slots,
+                            const int32_t* layer_slot, const int32_t* layer_window,
+                            float softmax_scale, void* stream);
+
+/*
  * mqa_hbm_read_probe -- a streaming read of device memory, to measure the
  * bandwidth a plain read reaches on this GPU (decode attention streams KV
  * bytes, whose volume sets its cost: Character.AI page, section 02).  Not

@@ -33,7 +33,7 @@ import torch  # noqa: F401  (import order matters, see above)
 __all__ = [
     "PAGE_TOKENS", "MQAError", "KVPool", "lib", "page_bytes", "kv_bytes_per_token",
     "page_layout", "kv_pack_int8", "decode_workspace_bytes", "decode_workspace",
-    "mqa_decode_attn", "mqa_decode_step",
+    "mqa_decode_attn", "mqa_decode_step", "mqa_decode_step_noalloc", "DECODE_STATIC_SCRATCH_BYTES",
     "mqa_append_attn", "slot_mapping_for", "unpack_page_tokens",
     "kv_footprint_bytes", "PageTable", "PrefixCache",
     "gqa_page_bytes", "gqa_pack_bf16", "gqa_decode_workspace", "gqa_decode_bf16",
@@ -84,6 +84,10 @@ def _load() -> ctypes.CDLL:
     L.mqa_decode_step.argtypes = [p, ctypes.c_int, p, p, p, ctypes.c_int, ctypes.POINTER(_Pool), p,
                                   i32, p, i32, i32, i32, i32, i32, p, p, f32, p, sz, p]
     L.mqa_decode_step.restype = ctypes.c_int
+    L.mqa_decode_step_noalloc.argtypes = [p, ctypes.c_int, p, p, p, ctypes.c_int,
+                                          ctypes.POINTER(_Pool), p, i32, p, i32, i32, i32, i32,
+                                          i32, p, p, f32, p]
+    L.mqa_decode_step_noalloc.restype = ctypes.c_int
     L.mqa_append_attn.argtypes = [p, ctypes.c_int, p, ctypes.POINTER(_Pool), p, i32, p, p, i32,
                                   i32, i32, i32, i32, i32, i32, p, p, f32, p]
     L.mqa_append_attn.restype = ctypes.c_int
@@ -614,6 +618,30 @@ def mqa_decode_step(q, out, k_new, v_new, pool: KVPool, block_table, context_len
         int(block_table.shape[2]), cl_p, int(max_context), batch, hq, n_layers, num_slots,
         ls.ctypes.data, lw.ctypes.data, float(softmax_scale), ws_ptr, ws_bytes,
         _stream_ptr(stream)))
+
+
+DECODE_STATIC_SCRATCH_BYTES = 40 << 20
+
+
+def mqa_decode_step_noalloc(q, out, k_new, v_new, pool: KVPool, block_table, context_lens,
+                            max_context: int, layer_slot: Sequence[int],
+                            layer_window: Sequence[int], softmax_scale: float = 0.0,
+                            stream=None) -> None:
+    """:func:`mqa_decode_step` with no workspace: its scratch is the library's
+    static per-GPU array (calls that overlap on one GPU race)."""
+    (n_layers, batch, hq, ls, lw, _, _, out_p, bt_p,
+     cl_p) = _decode_args(q, out, pool, block_table, context_lens, layer_slot, layer_window, None)
+    num_slots = int(block_table.shape[0])
+    want = (num_slots, batch, pool.head_dim)
+    if tuple(k_new.shape) != want or tuple(v_new.shape) != want:
+        raise ValueError(f"k_new and v_new must be {list(want)}")
+    if k_new.dtype != v_new.dtype:
+        raise ValueError("k_new and v_new must have the same dtype")
+    _check(lib.mqa_decode_step_noalloc(
+        _dev_ptr(q, "q"), _dtype_code(q), out_p, _dev_ptr(k_new, "k_new"),
+        _dev_ptr(v_new, "v_new"), _dtype_code(k_new), ctypes.byref(pool.c), bt_p,
+        int(block_table.shape[2]), cl_p, int(max_context), batch, hq, n_layers, num_slots,
+        ls.ctypes.data, lw.ctypes.data, float(softmax_scale), _stream_ptr(stream)))
 
 
 def mqa_append_attn(q, out, pool: KVPool, block_table, context_lens, cu_q_lens, max_context: int,

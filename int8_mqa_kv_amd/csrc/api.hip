@@ -7,6 +7,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -410,14 +412,21 @@ int mqa_decode_tuning(int32_t waves, int32_t rows, int32_t target_wgs) {
 
 namespace {
 
-// Shared by mqa_decode_attn and mqa_decode_step.
+// Supplies the workspace of a decode call from somewhere other than the
+// caller (the static scratch of mqa_decode_step_noalloc): called after every
+// host check has passed and before the launch, with the bytes the plan needs
+// (0 if none); sets *ws and returns MQA_OK, or a status that ends the call.
+typedef int (*WorkspaceSource)(size_t need, void** ws, hipStream_t stream);
+
+// Shared by mqa_decode_attn, mqa_decode_step and mqa_decode_step_noalloc.
 int decode_common(const void* q, mqa_dtype q_dtype, float* out, const void* k_new,
                   const void* v_new, NewKV nk, const mqa_kv_pool* pool,
                   const int32_t* block_table, int32_t max_pages_per_seq,
                   const int32_t* context_lens, int32_t max_context, int32_t batch,
                   int32_t num_q_heads, int32_t num_layers, int32_t num_slots,
                   const int32_t* layer_slot, const int32_t* layer_window, float softmax_scale,
-                  void* workspace, size_t workspace_bytes, void* stream, const char* what) {
+                  void* workspace, size_t workspace_bytes, void* stream, const char* what,
+                  WorkspaceSource source = nullptr) {
   int rc = check_attn_common(q, q_dtype, out, pool, block_table, max_pages_per_seq, context_lens,
                              max_context, batch, num_q_heads, num_layers, num_slots, layer_slot,
                              layer_window);
@@ -425,6 +434,11 @@ int decode_common(const void* q, mqa_dtype q_dtype, float* out, const void* k_ne
   DecodePlan p = plan_decode_auto(batch, num_q_heads, num_layers, layer_slot, layer_window,
                                   max_context, pool->head_dim, q_dtype == MQA_F32);
   if (p.rc) return p.rc;
+  if (source) {
+    rc = source(p.ws_bytes, &workspace, static_cast<hipStream_t>(stream));
+    if (rc) return rc;
+    workspace_bytes = p.ws_bytes;
+  }
   if (p.ws_bytes > 0) {
     if (!workspace || workspace_bytes < p.ws_bytes)
       return fail(MQA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.ws_bytes,
@@ -566,6 +580,98 @@ int mqa_hbm_read_probe(const void* src, int64_t bytes, uint32_t* sink, int32_t s
                                  static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mqa_hbm_read_probe launch");
   return ok();
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// mqa_decode_step_noalloc: mqa_decode_step with its workspace in a static
+// device array of this library (one copy per GPU, held until the process
+// ends), for callers that cannot allocate device memory.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[MQA_DECODE_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Per device: the address of that device's copy of `scratch` (the array's
+// name is a host-side stand-in, never a device address) and whether its
+// arrival counters have been cleared once.
+struct StaticScratch {
+  std::once_flag once;
+  hipError_t err = hipSuccess;
+  void* ptr = nullptr;
+  std::atomic<bool> cleared{false};
+};
+StaticScratch g_static_scratch[kMaxDevices];
+
+__global__ void zero_words_kernel(uint32_t* __restrict__ p, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0;
+}
+
+// The workspace source of mqa_decode_step_noalloc.  The first call on a
+// device looks up that device's copy of `scratch` (with the device current).
+// The arrival counters at its head must start at zero; every decode call
+// leaves them at zero again, so they are cleared by a fill kernel on the
+// caller's stream before the first decode that uses them (again on every
+// call made while the stream is being captured, so that a graph captured
+// first still clears them before its decode when replayed).  A fill kernel,
+// not hipMemsetAsync, so that the clear can sit in a captured graph.
+int static_scratch_source(size_t need, void** ws, hipStream_t stream) {
+  if (need > (size_t)MQA_DECODE_STATIC_SCRATCH_BYTES)
+    return fail(MQA_ERR_WORKSPACE,
+                "this launch needs %zu bytes of decode scratch; the static scratch of "
+                "mqa_decode_step_noalloc holds %zu (use mqa_decode_step with a workspace)",
+                need, (size_t)MQA_DECODE_STATIC_SCRATCH_BYTES);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MQA_ERR_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", dev,
+                kMaxDevices - 1);
+  StaticScratch& s = g_static_scratch[dev];
+  std::call_once(s.once, [&] { s.err = hipGetSymbolAddress(&s.ptr, HIP_SYMBOL(scratch)); });
+  if (s.err != hipSuccess) return hip_fail(s.err, "hipGetSymbolAddress(scratch)");
+  if (!s.ptr) return fail(MQA_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+  *ws = s.ptr;
+  if (need == 0 || s.cleared.load(std::memory_order_acquire)) return MQA_OK;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  e = hipStreamIsCapturing(stream, &cap);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+  hipLaunchKernelGGL(zero_words_kernel, dim3(1024), dim3(256), 0, stream,
+                     static_cast<uint32_t*>(s.ptr), kCounterWords);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "clearing the static decode scratch");
+  if (cap == hipStreamCaptureStatusNone) s.cleared.store(true, std::memory_order_release);
+  return MQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mqa_decode_step_noalloc(const void* q, mqa_dtype q_dtype, float* out, const void* k_new,
+                            const void* v_new, mqa_dtype kv_dtype, const mqa_kv_pool* pool,
+                            const int32_t* block_table, int32_t max_pages_per_seq,
+                            const int32_t* context_lens, int32_t max_context, int32_t batch,
+                            int32_t num_q_heads, int32_t num_layers, int32_t num_slots,
+                            const int32_t* layer_slot, const int32_t* layer_window,
+                            float softmax_scale, void* stream) {
+  static_assert(MQA_DECODE_STATIC_SCRATCH_BYTES > kCounterWords * sizeof(float),
+                "the static scratch holds the arrival counters and partial records");
+  if (kv_dtype != MQA_F32 && kv_dtype != MQA_BF16)
+    return fail(MQA_ERR_UNSUPPORTED, "k_new/v_new dtype %d unsupported", (int)kv_dtype);
+  if (!k_new || !v_new) return fail(MQA_ERR_INVALID, "k_new and v_new must be non-NULL");
+  const size_t esz = kv_dtype == MQA_BF16 ? 2 : 4;
+  if (!aligned(k_new, esz) || !aligned(v_new, esz))
+    return fail(MQA_ERR_INVALID, "misaligned k_new or v_new");
+  return decode_common(q, q_dtype, out, k_new, v_new,
+                       kv_dtype == MQA_BF16 ? NewKV::kBf16 : NewKV::kF32, pool, block_table,
+                       max_pages_per_seq, context_lens, max_context, batch, num_q_heads,
+                       num_layers, num_slots, layer_slot, layer_window, softmax_scale, nullptr, 0,
+                       stream, "mqa_decode_step_noalloc launch", static_scratch_source);
 }
 
 }  // extern "C"

@@ -206,3 +206,17 @@ def test_probe_rejects_bad_arguments():
     assert rc == mk.MQA_ERR_INVALID and "aligned" in mk.lib.mqa_last_error().decode()
     rc = mk.lib.mqa_hbm_read_probe(None, 4096, 0x2000, mk.PROBE_SINK_WORDS, None)
     assert rc == mk.MQA_ERR_INVALID
+
+
+def test_noalloc_step_rejects_launches_beyond_its_scratch():
+    """mqa_decode_step_noalloc plans on the host and refuses a launch whose
+    scratch exceeds its static array before it touches the device."""
+    pool = mk._Pool(0x100000, 16, 128, 0)
+    ls, lw = np.zeros(1, np.int32), np.zeros(1, np.int32)
+    args = (0x1000, mk.MQA_BF16, 0x2000, 0x3000, 0x4000, mk.MQA_F32, ctypes.byref(pool), 0x5000,
+            1 << 14, 0x6000, 1 << 18, 256, 64, 1, 1, ls.ctypes.data, lw.ctypes.data, 0.0, None)
+    assert mk.lib.mqa_decode_step_noalloc(*args) == mk.MQA_ERR_WORKSPACE
+    assert "static scratch" in mk.lib.mqa_last_error().decode()
+    bad = list(args)
+    bad[5] = 7
+    assert mk.lib.mqa_decode_step_noalloc(*bad) == mk.MQA_ERR_UNSUPPORTED
