@@ -65,7 +65,14 @@ typedef enum {
   MQA_ERR_HIP = -4           /* the HIP runtime reported an error               */
 } mqa_status;
 
-typedef enum {
+/* A dtype argument is an int on the wire; entry points reject values other
+ * than these.  (C++ gives the enum int as its underlying type, so that an
+ * out-of-range value passed in is still a valid value to test and reject.) */
+#ifdef __cplusplus
+typedef enum mqa_dtype : int {
+#else
+typedef enum mqa_dtype {
+#endif
   MQA_F32 = 0,               /* IEEE binary32                                   */
   MQA_BF16 = 1               /* bfloat16 (upper half of a binary32)             */
 } mqa_dtype;

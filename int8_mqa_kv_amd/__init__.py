@@ -42,7 +42,9 @@ __all__ = [
 
 PAGE_TOKENS = 16
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmqa_kv.so")
+# MQA_KV_LIB selects another build of the library (the host-sanitizer build
+# of the CPU checks); by default the gfx950 build beside this file.
+LIB_PATH = os.environ.get("MQA_KV_LIB") or os.path.join(_HERE, "libmqa_kv.so")
 
 MQA_OK, MQA_ERR_INVALID, MQA_ERR_UNSUPPORTED, MQA_ERR_WORKSPACE, MQA_ERR_HIP = 0, -1, -2, -3, -4
 MQA_F32, MQA_BF16 = 0, 1

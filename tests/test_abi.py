@@ -3,6 +3,7 @@ rejects bad arguments before touching the GPU (no compute calls here)."""
 import ctypes
 import os
 import re
+import subprocess
 
 import numpy as np
 import pytest
@@ -220,3 +221,13 @@ def test_noalloc_step_rejects_launches_beyond_its_scratch():
     bad = list(args)
     bad[5] = 7
     assert mk.lib.mqa_decode_step_noalloc(*bad) == mk.MQA_ERR_UNSUPPORTED
+
+
+def test_header_compiles_as_c_and_cpp():
+    """include/mqa_kv.h is a C header usable from C11 and C++17 callers."""
+    hdr = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                       "mqa_kv.h")
+    for cmd in (["gcc", "-std=c11", "-Wall", "-Wextra", "-pedantic", "-fsyntax-only", "-x", "c", hdr],
+                ["g++", "-std=c++17", "-Wall", "-Wextra", "-fsyntax-only", "-x", "c++", hdr]):
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        assert r.returncode == 0 and not r.stderr.strip(), r.stderr
