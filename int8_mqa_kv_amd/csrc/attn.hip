@@ -857,6 +857,7 @@ __global__ __launch_bounds__(W * 64, 2) void decode_kernel(
   const int lo = sp.lo, hi = sp.hi;
 
   if (hi <= lo) {  // empty context: zeros (and no current token to store)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // (the staged q rows land first)
     if (chunk == 0 && wv == 0) {
       for (int n = 0; n < NRT; ++n) {
         const int row = 16 * n + li;
@@ -869,7 +870,10 @@ __global__ __launch_bounds__(W * 64, 2) void decode_kernel(
     return;
   }
   const int nch = sp.nch, p_last = sp.p_last;
-  if (chunk >= nch) return;
+  if (chunk >= nch) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    return;
+  }
   // (wave-uniform: in scalar registers, so that the loop's page checks are
   // scalar instructions)
   const int pbeg = __builtin_amdgcn_readfirstlane(sp.pbeg);

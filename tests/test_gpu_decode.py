@@ -198,9 +198,8 @@ def test_loose_host_context_bound(windows):
 
 @pytest.mark.parametrize("window", [0, 300], ids=["global", "window300"])
 def test_many_ragged_sequences(window):
-    """130 sequences of ragged lengths (1 to 1500 tokens): the kernel reads the
-    lengths 64 at a time and shares its workgroups out over the sequences in
-    chunks sized from the true page counts."""
+    """130 sequences of ragged lengths (1 to 1500 tokens), one workgroup per
+    (row block, sequence)."""
     ctx = [1 + (37 * i * i + 11 * i) % 1500 for i in range(130)]
     w = synth.custom_decode(20 + (window > 0), 130, 32, 128, "bf16", ctx, 1, window, 0)
     _run_case(w)
@@ -237,3 +236,52 @@ def test_outlier_query_channels(gain, window):
     out = g.decode(q)
     want = oracle.decode(q64, w.context_lens, w.layer_slot, w.layer_window, OracleKV(w))
     assert_parity(out.cpu().numpy(), want, f"outlier q x{gain}, window {window}")
+
+
+RAGGED_GLOBAL = {
+    # 24 global sequences from 0 to 32768 tokens (empty, single-token, page
+    # edges), permuted pool: the longest set the chunk boundaries, the
+    # shorter fill fewer chunks
+    "lengths_0_to_32k": lambda: synth.custom_decode(
+        30, 24, 32, 128, "bf16", [0, 1, 15, 16, 17, 300, 1024, 4095, 4096, 4097, 8000, 16000, 32768,
+                                  2, 33, 5000, 12000, 20000, 31000, 100, 7, 64, 65, 9999], 1, 0,
+        permuted_pool=40000),
+    # 100 sequences of 1 to 6000 tokens, two chunks each at most
+    "batch100": lambda: synth.custom_decode(
+        31, 100, 32, 128, "bf16", [1 + (53 * i * i + 7 * i) % 6000 for i in range(100)], 1, 0,
+        permuted_pool=40000),
+    # fp32 q, two layers on one slot (two 16-row blocks each), 40 sequences
+    "f32_two_layers": lambda: synth.custom_decode(
+        32, 40, 32, 128, "f32", [17 + (97 * i) % 9000 for i in range(40)], 2, 0,
+        permuted_pool=30000),
+}
+
+
+def _run_with_empty(w):
+    """Parity on the sequences with a context; zeros (the header's rule for a
+    length <= 0) on the others."""
+    full = [b for b in range(w.batch) if w.context_lens[b] > 0]
+    empty = [b for b in range(w.batch) if w.context_lens[b] <= 0]
+    _, _, out, _ = _run_case(w, seqs=full)
+    if empty:
+        assert torch.all(out[:, empty] == 0)
+
+
+@pytest.mark.parametrize("name", list(RAGGED_GLOBAL))
+def test_ragged_global_lengths(name):
+    """Global groups split into chunks over sequences of very different
+    lengths, empty ones included."""
+    _run_with_empty(RAGGED_GLOBAL[name]())
+
+
+def test_many_sequences_split():
+    """200 sequences (0 to 3000 tokens), split into chunks because the
+    workgroup target is raised to 1024."""
+    mk.decode_tuning(target_wgs=1024)
+    try:
+        w = synth.custom_decode(33, 200, 32, 128, "bf16",
+                                [(41 * i * i + 3 * i) % 3000 for i in range(200)], 1, 0,
+                                permuted_pool=40000)
+        _run_with_empty(w)
+    finally:
+        mk.decode_tuning()
