@@ -768,7 +768,7 @@ def summarize_counters(case, d, cmds):
             v = cs.get(counter, [])
             if not v:
                 continue
-            name = k.split("(")[0].replace("void ", "")
+            name = k.replace("void ", "").split(">(")[0] + ">"
             mean = float(np.mean(v))
             out["kernels"].setdefault(name, {})[counter] = {"mean_units": mean,
                                                              "bytes": mean * scale,
