@@ -175,9 +175,12 @@ size_t mqa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
 
 /*
  * Decode tuning (not part of what is computed: results depend on it only
- * through the rounding order of the merges).  Process-wide; not thread-safe
- * against concurrent decode calls or workspace queries.  Each argument is 0
- * for "the planner decides" or a forced value:
+ * through the rounding order of the merges).  Process-wide: a change applies
+ * to every later call from any thread (each value is stored atomically; a call
+ * racing with a change plans with the old or the new value of each), and a
+ * workspace sized before a change may be too small after it.  Meant for tests
+ * and tuning, not for a serving loop.  Each argument is 0 for "the planner
+ * decides" or a forced value:
  *  waves       wavefronts per decode workgroup: 8 (one workgroup per CU) or
  *              4 (two per CU).  The planner takes 4 only when the 8-wavefront
  *              plan leaves more than 15 % of the CUs idle while splitting

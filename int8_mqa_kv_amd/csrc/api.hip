@@ -122,29 +122,34 @@ struct DecodePlan {
 // Decode tuning overrides (0 = the planner decides), process-wide.  They start
 // from MQA_DECODE_WAVES (4 or 8), MQA_DECODE_ROWS (8, 16 or 32) and
 // MQA_DECODE_TARGET_WGS, and mqa_decode_tuning() replaces them.  Results do
-// not depend on them beyond rounding order.
+// not depend on them beyond rounding order.  Each value is one atomic, so a
+// change racing with a call is no data race; that call plans with the old or
+// the new value of each.
 struct DecodeTuning {
-  int waves = 0, rows = 0, target_wgs = 0;
+  std::atomic<int> waves{0}, rows{0}, target_wgs{0};
 };
 DecodeTuning& tuning() {
-  static DecodeTuning t = [] {
-    DecodeTuning d;
+  static DecodeTuning t;
+  static std::once_flag once;
+  std::call_once(once, [] {
     auto env = [](const char* name) {
       const char* e = getenv(name);
       return e ? atoi(e) : 0;
     };
     const int w = env("MQA_DECODE_WAVES"), r = env("MQA_DECODE_ROWS"), g = env("MQA_DECODE_TARGET_WGS");
-    d.waves = (w == kDecodeWaves || w == kDecodeWavesSmall) ? w : 0;
-    d.rows = (r == 8 || r == 16 || r == 32) ? r : 0;
-    d.target_wgs = g > 0 ? g : 0;
-    return d;
-  }();
+    t.waves = (w == kDecodeWaves || w == kDecodeWavesSmall) ? w : 0;
+    t.rows = (r == 8 || r == 16 || r == 32) ? r : 0;
+    t.target_wgs = g > 0 ? g : 0;
+  });
   return t;
 }
 
 // Workgroups of kDecodeWaves wavefronts the planner aims for: one per compute
 // unit of the 256 (twice as many of the four-wavefront shape).
-int target_workgroups() { return tuning().target_wgs > 0 ? tuning().target_wgs : 256; }
+int target_workgroups() {
+  const int g = tuning().target_wgs;
+  return g > 0 ? g : 256;
+}
 int decode_rows_override() { return tuning().rows; }
 
 // Query rows per row block.  32 rows (two 16-row tiles per wavefront) read
@@ -297,9 +302,10 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
 DecodePlan plan_decode_auto(int32_t batch, int32_t num_q_heads, int32_t num_layers,
                             const int32_t* layer_slot, const int32_t* layer_window,
                             int32_t max_context, int32_t head_dim, bool q_f32) {
-  if (tuning().waves)
+  const int forced_waves = tuning().waves;
+  if (forced_waves)
     return plan_decode(batch, num_q_heads, num_layers, layer_slot, layer_window, max_context,
-                       head_dim, q_f32, tuning().waves);
+                       head_dim, q_f32, forced_waves);
   DecodePlan p8 = plan_decode(batch, num_q_heads, num_layers, layer_slot, layer_window,
                               max_context, head_dim, q_f32, kDecodeWaves);
   if (p8.rc) return p8;
