@@ -447,28 +447,6 @@ def hbm_probe(torch, mk, sizes, total=2 << 30, launches=40):
         out[str(size)] = {"bytes": size, "us_per_read": round(sec * 1e6, 3),
                           "gbs": round(size / sec / 1e9, 1),
                           "pct_of_8000": round(100 * size / sec / 1e9 / HBM_PEAK_GBS, 2)}
-    # The same kernel re-reading one 16 MiB slice: after the first read each
-    # XCD's 4 MB L2 holds its workgroups' share (2 MiB), so this is the rate
-    # at which the compute units take data in from L2.
-    res = buf[:16 << 20]
-    mk.hbm_read_probe(res, sink)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for _ in range(launches):
-            mk.hbm_read_probe(res, sink)
-    g.replay()
-    torch.cuda.synchronize()
-    E = torch.cuda.Event
-    e0, e1 = E(enable_timing=True), E(enable_timing=True)
-    e0.record()
-    g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    sec = e0.elapsed_time(e1) * 1e-3 / launches
-    l2 = {"bytes": res.numel(), "us_per_read": round(sec * 1e6, 3),
-          "gbs": round(res.numel() / sec / 1e9, 1),
-          "gbs_per_cu": round(res.numel() / sec / 1e9 / 256, 1)}
     # the probe's own check: the XOR of the sink words is that of the buffer
     mk.hbm_read_probe(buf[:1 << 20], sink)
     got = int(np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)))
@@ -476,7 +454,7 @@ def hbm_probe(torch, mk, sizes, total=2 << 30, launches=40):
     del buf, sink
     torch.cuda.empty_cache()
     return {"kernel": "hbm_read_kernel (mqa_hbm_read_probe): 128-bit loads, 8 in flight per lane",
-            "by_size": out, "l2_resident_16MiB": l2, "xor_check": got == want}
+            "by_size": out, "xor_check": got == want}
 
 
 def main():
