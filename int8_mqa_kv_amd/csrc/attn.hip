@@ -210,17 +210,27 @@ struct WaveState {
   float m[NRT];                // running max (log2 domain), equal on a row's 4 lanes
   float l[NRT];                // this lane's part of the row's running sum
   int ev;                      // exponent of the largest V scale seen (kNoExp: none)
+  // Cached from the last time the reference or the V exponent moved: a key
+  // scale times score above thr[n] moves row n's reference; a V scale at or
+  // above ev_thr = 2^ev moves the exponent; neg_m = -m (0 for -inf);
+  // pvm = 2^(kPvBias - ev) (0 while no V scale was seen).
+  float thr[NRT], neg_m[NRT];
+  float ev_thr, pvm;
 
   __device__ __forceinline__ void init() {
 #pragma unroll
     for (int n = 0; n < NRT; ++n) {
       m[n] = kNegInf;
       l[n] = 0.0f;
+      thr[n] = kNegInf;
+      neg_m[n] = 0.0f;
       psum[n] = f32x4{0, 0, 0, 0};
 #pragma unroll
       for (int t = 0; t < Geo<D>::VT; ++t) acc[n][t] = f32x4{0, 0, 0, 0};
     }
     ev = kNoExp;
+    ev_thr = 0.0f;
+    pvm = 0.0f;
   }
   // The accumulators hold P.(V codes + kCodeBias): remove kCodeBias * sum(P).
   __device__ __forceinline__ void unbias() {
@@ -238,7 +248,13 @@ struct WaveState {
 // exceeds it by more than kTau (log2 units), so p = exp2(sigma - m_ref) stays
 // below 2^kTau and most blocks skip rescaling the accumulators.  P*sV is then
 // scaled by 2^(kPvBias - ev) (ev: exponent of the largest V scale seen), which
-// keeps the fp16 P operand below 2^14.
+// keeps the fp16 P operand below 2^14.  Both conditions are tested first
+// against thresholds cached when the reference last moved (a key's score
+// times its scale, and a V scale, each compared in its own lane); only a block
+// that passes one works out row maxima across lanes and the new references.
+// (Where the threshold test and the reference test round differently, p may
+// exceed 2^kTau by a rounding, or a block takes the full path and moves
+// nothing; results stay deterministic.)
 constexpr float kTau = 8.0f;
 constexpr int kPvBias = 14 - 8;
 
@@ -284,7 +300,14 @@ __device__ __forceinline__ void attend_block(WaveState<D, NRT>& st, const QOps<D
       valid[u][r] = !MASKED || ((u ? ok1 : ok0) && pos >= lo && pos < hi);
     }
 
-  // Largest valid V scale of the block -> running exponent (wave-uniform).
+  // t = score * key scale (-inf for a masked key); the row's factor crow
+  // (> 0) is applied in the exponent's FMA.  First the cheap test: does any
+  // key move a row's reference (t above the row's cached threshold) or the V
+  // exponent (a valid V scale at or above 2^ev)?  Only then (wave-uniform,
+  // rare after a row's first blocks) are the row maxima, the new references
+  // and the rescale worked out.
+  float t[NRT][2][4];
+  float lmax[NRT];
   float vmax = 0.0f;
 #pragma unroll
   for (int u = 0; u < 2; ++u)
@@ -293,26 +316,9 @@ __device__ __forceinline__ void attend_block(WaveState<D, NRT>& st, const QOps<D
       const float sv = (u ? p1.sv : p0.sv)[r];
       vmax = fmaxf(vmax, MASKED ? (valid[u][r] ? sv : 0.0f) : sv);
     }
-  vmax = row_max4(vmax);
-  int ev_new = st.ev;
-  // (clamped so that 2^(kPvBias-ev) stays finite for absurdly small scales)
-  if (vmax > 0.0f) ev_new = max(ev_new, max(frexp_exp(vmax), -100));
-  const int dexp = st.ev == kNoExp ? 0 : st.ev - ev_new;
-  st.ev = ev_new;
-  const float pvm = ev_new == kNoExp ? 0.0f : ldexp2(1.0f, kPvBias - ev_new);
-
-  // Row maxima and the lazy reference first: whether the accumulators need
-  // rescaling is known before any exponent, so the rescale branch comes
-  // before the exponents and the PV products, which then share one block of
-  // code (the P of one row tile is computed while the other tile's PV
-  // products run on the matrix cores).
-  float t[NRT][2][4];
-  float alpha[NRT], neg_m[NRT];
-  bool rescale = false;
+  bool moves = vmax >= st.ev_thr;
 #pragma unroll
   for (int n = 0; n < NRT; ++n) {
-    // t = int score * key scale; the row's factor crow (> 0) is applied in
-    // the exponent's FMA, so the row max is taken on t
     float mt = kNegInf;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
@@ -322,26 +328,51 @@ __device__ __forceinline__ void attend_block(WaveState<D, NRT>& st, const QOps<D
         t[n][u][r] = MASKED ? (valid[u][r] ? x : kNegInf) : x;
         mt = fmaxf(mt, t[n][u][r]);
       }
-    mt = row_max4(mt);
-    const float mx = mt == kNegInf ? kNegInf : mt * q.crow[n];
-    const bool move = mx > st.m[n] + kTau;  // also true for the first valid block
-    const float m_new = move ? mx : st.m[n];
-    alpha[n] = move ? fast_exp2(st.m[n] - m_new) : 1.0f;  // exp2(-inf) = 0
-    rescale |= move;
-    neg_m[n] = m_new == kNegInf ? 0.0f : -m_new;
-    st.m[n] = m_new;
+    lmax[n] = mt;
+    moves |= mt > st.thr[n];
   }
-  // rescale the accumulators only when some row's reference moved or the V
-  // exponent grew (wave-uniform branch)
-  if (__builtin_amdgcn_ballot_w64(rescale) != 0 || dexp != 0) {
+  float alpha[NRT];
+#pragma unroll
+  for (int n = 0; n < NRT; ++n) alpha[n] = 1.0f;
+  if (__builtin_amdgcn_ballot_w64(moves) != 0) {  // wave-uniform
+    // Largest valid V scale of the block -> running exponent.
+    const float vm = row_max4(vmax);
+    int ev_new = st.ev;
+    // (clamped so that 2^(kPvBias-ev) stays finite for absurdly small scales)
+    if (vm > 0.0f) ev_new = max(ev_new, max(frexp_exp(vm), -100));
+    const int dexp = st.ev == kNoExp ? 0 : st.ev - ev_new;
+    st.ev = ev_new;
+    st.pvm = ev_new == kNoExp ? 0.0f : ldexp2(1.0f, kPvBias - ev_new);
+    st.ev_thr = ev_new == kNoExp ? 0.0f : ldexp2(1.0f, ev_new);
+    bool rescale = false;
 #pragma unroll
     for (int n = 0; n < NRT; ++n) {
-      const float f = ldexp2(alpha[n], dexp);
+      const float mt = row_max4(lmax[n]);
+      const float mx = mt == kNegInf ? kNegInf : mt * q.crow[n];
+      const bool move = mx > st.m[n] + kTau;  // also true for the first valid block
+      const float m_new = move ? mx : st.m[n];
+      alpha[n] = move ? fast_exp2(st.m[n] - m_new) : 1.0f;  // exp2(-inf) = 0
+      rescale |= move;
+      st.neg_m[n] = m_new == kNegInf ? 0.0f : -m_new;
+      st.thr[n] = m_new == kNegInf ? kNegInf : (m_new + kTau) / q.crow[n];
+      st.m[n] = m_new;
+    }
+    // rescale the accumulators only when some row's reference moved or the
+    // V exponent grew (wave-uniform branch)
+    if (__builtin_amdgcn_ballot_w64(rescale) != 0 || dexp != 0) {
 #pragma unroll
-      for (int t = 0; t < Geo<D>::VT; ++t) st.acc[n][t] *= f;
-      st.psum[n] *= f;
+      for (int n = 0; n < NRT; ++n) {
+        const float f = ldexp2(alpha[n], dexp);
+#pragma unroll
+        for (int t = 0; t < Geo<D>::VT; ++t) st.acc[n][t] *= f;
+        st.psum[n] *= f;
+      }
     }
   }
+  const float pvm = st.pvm;
+  float neg_m[NRT];
+#pragma unroll
+  for (int n = 0; n < NRT; ++n) neg_m[n] = st.neg_m[n];
 
   // P*sV as two fp16 terms, hi and lo (hi + lo within 2^-22 of it)
   f16x8 ph[NRT], pl[NRT];
