@@ -200,6 +200,26 @@ __device__ __forceinline__ void convert_q(QOps<D, QS, NRT>& o, const QRaw<D, QS,
   }
 }
 
+// Lazy softmax reference: a row's reference max only moves when a block's max
+// exceeds it by more than kTau (log2 units), so p = exp2(sigma - m_ref) stays
+// below 2^kTau and most blocks skip rescaling the accumulators.  The weights
+// are formed already multiplied by 2^lpv, lpv = kPvBias - ev (ev: exponent of
+// the largest V scale seen; lpv = 0 while none was seen), through the
+// exponent's offset: P*sV then stays below 2^14 as an fp16 operand, and the
+// running sum l is kept in the same units until the key loop ends.  Both
+// conditions are tested first against thresholds cached when the reference
+// last moved (a key's score times its scale, and a V scale, each compared in
+// its own lane); only a block that passes one works out row maxima across
+// lanes and the new references.  (Where the threshold test and the reference
+// test round differently, p may exceed 2^kTau by a rounding, or a block takes
+// the full path and moves nothing; results stay deterministic.)
+constexpr float kTau = 8.0f;
+constexpr int kPvBias = 14 - 8;
+// Smallest V exponent tracked: keeps 2^lpv, and l in its units, finite for
+// absurdly small scales (a V scale below 2^-64 contributes below 2^-57 to any
+// output).
+constexpr int kMinVExp = -64;
+
 // ---------------------------------------------------------------------------
 // One wavefront's running softmax state over its keys
 // ---------------------------------------------------------------------------
@@ -208,14 +228,15 @@ struct WaveState {
   f32x4 acc[NRT][Geo<D>::VT];  // O^T tiles: lane (i, g) holds channels 16t+4g..+3 of row i
   f32x4 psum[NRT];             // sum of the P operand over keys, row i (all 4 equal)
   float m[NRT];                // running max (log2 domain), equal on a row's 4 lanes
-  float l[NRT];                // this lane's part of the row's running sum
+  float l[NRT];                // this lane's part of the row's running sum, in units of
+                               // 2^lpv during the key loop (plain after finish())
   int ev;                      // exponent of the largest V scale seen (kNoExp: none)
   // Cached from the last time the reference or the V exponent moved: a key
   // scale times score above thr[n] moves row n's reference; a V scale at or
-  // above ev_thr = 2^ev moves the exponent; neg_m = -m (0 for -inf);
-  // pvm = 2^(kPvBias - ev) (0 while no V scale was seen).
-  float thr[NRT], neg_m[NRT];
-  float ev_thr, pvm;
+  // above ev_thr = 2^ev moves the exponent; off[n] = lpv - m (lpv for
+  // m = -inf) is the exponent's offset.
+  float thr[NRT], off[NRT];
+  float ev_thr;
 
   __device__ __forceinline__ void init() {
 #pragma unroll
@@ -223,40 +244,29 @@ struct WaveState {
       m[n] = kNegInf;
       l[n] = 0.0f;
       thr[n] = kNegInf;
-      neg_m[n] = 0.0f;
+      off[n] = 0.0f;
       psum[n] = f32x4{0, 0, 0, 0};
 #pragma unroll
       for (int t = 0; t < Geo<D>::VT; ++t) acc[n][t] = f32x4{0, 0, 0, 0};
     }
     ev = kNoExp;
     ev_thr = 0.0f;
-    pvm = 0.0f;
   }
-  // The accumulators hold P.(V codes + kCodeBias): remove kCodeBias * sum(P).
-  __device__ __forceinline__ void unbias() {
+  // After the last key: the accumulators hold P.(V codes + kCodeBias), so
+  // kCodeBias * sum(P) comes out; l returns from units of 2^lpv.
+  __device__ __forceinline__ void finish() {
+    const float u = ev == kNoExp ? 1.0f : ldexp2(1.0f, ev - kPvBias);
 #pragma unroll
-    for (int n = 0; n < NRT; ++n)
+    for (int n = 0; n < NRT; ++n) {
+      l[n] *= u;
 #pragma unroll
       for (int t = 0; t < Geo<D>::VT; ++t)
 #pragma unroll
         for (int k = 0; k < 4; ++k)
           acc[n][t][k] = __builtin_fmaf(-kCodeBias, psum[n][k], acc[n][t][k]);
+    }
   }
 };
-
-// Lazy softmax reference: a row's reference max only moves when a block's max
-// exceeds it by more than kTau (log2 units), so p = exp2(sigma - m_ref) stays
-// below 2^kTau and most blocks skip rescaling the accumulators.  P*sV is then
-// scaled by 2^(kPvBias - ev) (ev: exponent of the largest V scale seen), which
-// keeps the fp16 P operand below 2^14.  Both conditions are tested first
-// against thresholds cached when the reference last moved (a key's score
-// times its scale, and a V scale, each compared in its own lane); only a block
-// that passes one works out row maxima across lanes and the new references.
-// (Where the threshold test and the reference test round differently, p may
-// exceed 2^kTau by a rounding, or a block takes the full path and moves
-// nothing; results stay deterministic.)
-constexpr float kTau = 8.0f;
-constexpr int kPvBias = 14 - 8;
 
 // Attend the 32 keys of two consecutive logical pages.  pos0 is the position
 // of the first page's first token.  MASKED blocks (some key outside [lo, hi)
@@ -331,19 +341,17 @@ __device__ __forceinline__ void attend_block(WaveState<D, NRT>& st, const QOps<D
     lmax[n] = mt;
     moves |= mt > st.thr[n];
   }
-  float alpha[NRT];
-#pragma unroll
-  for (int n = 0; n < NRT; ++n) alpha[n] = 1.0f;
   if (__builtin_amdgcn_ballot_w64(moves) != 0) {  // wave-uniform
     // Largest valid V scale of the block -> running exponent.
     const float vm = row_max4(vmax);
     int ev_new = st.ev;
-    // (clamped so that 2^(kPvBias-ev) stays finite for absurdly small scales)
-    if (vm > 0.0f) ev_new = max(ev_new, max(frexp_exp(vm), -100));
-    const int dexp = st.ev == kNoExp ? 0 : st.ev - ev_new;
+    if (vm > 0.0f) ev_new = max(ev_new, max(frexp_exp(vm), kMinVExp));
+    const int lpv_old = st.ev == kNoExp ? 0 : kPvBias - st.ev;
+    const int lpv = ev_new == kNoExp ? 0 : kPvBias - ev_new;
+    const int dexp = lpv - lpv_old;  // the units of acc, psum and l change by 2^dexp
     st.ev = ev_new;
-    st.pvm = ev_new == kNoExp ? 0.0f : ldexp2(1.0f, kPvBias - ev_new);
     st.ev_thr = ev_new == kNoExp ? 0.0f : ldexp2(1.0f, ev_new);
+    float alpha[NRT];
     bool rescale = false;
 #pragma unroll
     for (int n = 0; n < NRT; ++n) {
@@ -353,12 +361,12 @@ __device__ __forceinline__ void attend_block(WaveState<D, NRT>& st, const QOps<D
       const float m_new = move ? mx : st.m[n];
       alpha[n] = move ? fast_exp2(st.m[n] - m_new) : 1.0f;  // exp2(-inf) = 0
       rescale |= move;
-      st.neg_m[n] = m_new == kNegInf ? 0.0f : -m_new;
+      st.off[n] = m_new == kNegInf ? (float)lpv : (float)lpv - m_new;
       st.thr[n] = m_new == kNegInf ? kNegInf : (m_new + kTau) / q.crow[n];
       st.m[n] = m_new;
     }
-    // rescale the accumulators only when some row's reference moved or the
-    // V exponent grew (wave-uniform branch)
+    // rescale only when some row's reference moved or the V exponent grew
+    // (wave-uniform branch)
     if (__builtin_amdgcn_ballot_w64(rescale) != 0 || dexp != 0) {
 #pragma unroll
       for (int n = 0; n < NRT; ++n) {
@@ -366,27 +374,28 @@ __device__ __forceinline__ void attend_block(WaveState<D, NRT>& st, const QOps<D
 #pragma unroll
         for (int t = 0; t < Geo<D>::VT; ++t) st.acc[n][t] *= f;
         st.psum[n] *= f;
+        st.l[n] *= f;
       }
     }
   }
-  const float pvm = st.pvm;
-  float neg_m[NRT];
+  float off[NRT];
 #pragma unroll
-  for (int n = 0; n < NRT; ++n) neg_m[n] = st.neg_m[n];
+  for (int n = 0; n < NRT; ++n) off[n] = st.off[n];
 
   // P*sV as two fp16 terms, hi and lo (hi + lo within 2^-22 of it)
   f16x8 ph[NRT], pl[NRT];
 #pragma unroll
   for (int n = 0; n < NRT; ++n) {
-    float ps = 0.0f;
+    float ps;
     float pv[8];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float pr = fast_exp2(__builtin_fmaf(t[n][u][r], q.crow[n], neg_m[n]));
-        ps += pr;
-        const float x = pr * ((u ? p1.sv : p0.sv)[r] * pvm);
+        // p * 2^lpv
+        const float pr = fast_exp2(__builtin_fmaf(t[n][u][r], q.crow[n], off[n]));
+        ps = u == 0 && r == 0 ? pr : ps + pr;
+        const float x = pr * (u ? p1.sv : p0.sv)[r];
         pv[4 * u + r] = MASKED ? (valid[u][r] ? x : 0.0f) : x;
       }
 #pragma unroll
@@ -398,7 +407,7 @@ __device__ __forceinline__ void attend_block(WaveState<D, NRT>& st, const QOps<D
       pl[n][e] = lo[0];
       pl[n][e + 1] = lo[1];
     }
-    st.l[n] = st.l[n] * alpha[n] + ps;
+    st.l[n] += ps;
   }
   // V codes enter as c + kCodeBias (two byte permutes per four codes); the
   // matching sum of P comes from products with an all-ones operand, so it
@@ -996,7 +1005,7 @@ __global__ __launch_bounds__(W * 64, 2) void decode_kernel(
     attend_block_any<D, QS, NRT>(st, q, c0, c1, ok0, ok1, pa * kPageTokens, lo, hi, lg);
   }
 
-  st.unbias();
+  st.finish();
   // ---- merge the W wavefronts: one LDS exchange ----
   // Every page load into this wavefront's ring has landed, so the wavefront
   // can dump its accumulators into its own ring without waiting for others.
@@ -1320,7 +1329,7 @@ __global__ __launch_bounds__(kAppendWaves * 64) void append_kernel(
   // every load of this wavefront has landed before the workgroup exits
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   if (!live) return;
-  st.unbias();
+  st.finish();
 #pragma unroll
   for (int n = 0; n < NRT; ++n) {
     const int row = 16 * n + li;

@@ -57,18 +57,17 @@ __device__ __forceinline__ f32x4 mma16(const f16x8& a, const f16x8& b, const f32
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// x - h for an fp32 value x and an fp16 value h held in the low (HI = false)
-// or high (HI = true) half of a packed register, in one mixed-precision FMA
-// (fp32 result, one rounding; exact when h is x rounded to fp16).
-template <bool HI>
-__device__ __forceinline__ float sub_f16_from(float x, f16x2 h) {
-  float r;
-  if constexpr (HI)
-    asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
-        : "=v"(r) : "v"(h), "v"(x));
-  else
-    asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x));
-  return r;
+// fp16(x - h) for an fp32 value x and an fp16 value h held in the low
+// (HI = false) or high (HI = true) half of a packed register, written into the
+// same half of d by one mixed-precision FMA (the rest is formed exactly and
+// rounded to fp16 once).  The low-half form leaves d's high half as it was,
+// the high-half form its low half.
+__device__ __forceinline__ void sub_f16_lo(uint32_t& d, float x, f16x2 h) {
+  asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(d) : "v"(h), "v"(x));
+}
+__device__ __forceinline__ void sub_f16_hi(uint32_t& d, float x, f16x2 h) {
+  asm("v_fma_mixhi_f16 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+      : "+v"(d) : "v"(h), "v"(x));
 }
 
 // Two fp32 values as a two-term fp16 pair each: hi = fp16(x) and
@@ -77,7 +76,10 @@ __device__ __forceinline__ float sub_f16_from(float x, f16x2 h) {
 // fp16's normal range is kept to fp16's subnormal spacing).
 __device__ __forceinline__ void split_f16x2(float x0, float x1, f16x2& hi, f16x2& lo) {
   hi = f16x2{(_Float16)x0, (_Float16)x1};
-  lo = f16x2{(_Float16)sub_f16_from<false>(x0, hi), (_Float16)sub_f16_from<true>(x1, hi)};
+  uint32_t r;
+  sub_f16_lo(r, x0, hi);
+  sub_f16_hi(r, x1, hi);
+  lo = bitcast<f16x2>(r);
 }
 
 // Reductions across the four lanes i, i+16, i+32, i+48 (one matrix row) with

@@ -5,6 +5,7 @@ the same workload, and compare outputs.
 Both sides start from the same seeded fp32 K/V rows and q values (``synth``);
 the GPU quantises with its own kernel, the oracle with its own quantiser.
 """
+import dataclasses
 import math
 import sys
 
@@ -177,3 +178,23 @@ def outlier_q(q, q64, gain, seed):
     q[..., torch.from_numpy(ch).to(q.device)] *= gain
     q64[..., ch] *= gain
     return q, q64
+
+
+class _VGain(synth.Workload):
+    """The workload with every V row multiplied by a power of two set by its
+    position: zero rows for positions below 40, 2^-80 up to position 300, then
+    2^-40 growing by one power of two every 128 positions up to 1.  A
+    wavefront's largest V scale so far thus starts absent, then sits far below
+    fp32's usual range, then grows again and again."""
+
+    def kv_rows(self, slot, seq, start, stop):
+        k, v = super().kv_rows(slot, seq, start, stop)
+        pos = np.arange(start, stop, dtype=np.int64)
+        e = np.where(pos < 300, -80, np.minimum(0, -40 + (pos - 300) // 128))
+        g = np.ldexp(np.float32(1), e.astype(np.int32)).astype(np.float32)
+        g[pos < 40] = 0
+        return k, v * g[:, None]
+
+
+def with_v_gain(w: synth.Workload) -> synth.Workload:
+    return _VGain(**{f.name: getattr(w, f.name) for f in dataclasses.fields(w)})

@@ -8,7 +8,7 @@ import torch
 import oracle
 import synth
 from tests.gpu_util import (MAX_ABS, REL_L2, GpuCase, OracleKV, assert_parity, log, outlier_q,
-                            q_tensor)
+                            q_tensor, with_v_gain)
 
 pytestmark = pytest.mark.gpu
 
@@ -123,3 +123,10 @@ def test_append_outlier_query_channels(gain):
     want = oracle.append(q64, w.context_lens, w.cu_q_lens, w.layer_slot, w.layer_window,
                          OracleKV(w))
     assert_parity(out.cpu().numpy(), want, f"append, outlier q x{gain}")
+
+
+def test_append_v_scales_over_many_octaves():
+    """Append over V rows that are zero, then 2^-80 of the usual size, then
+    growing by powers of two (see with_v_gain)."""
+    _run(with_v_gain(synth.custom_append(49, [20, 900, 3000], [30, 64, 17], 32, 128, [1024, 0],
+                                         [0, 1])))

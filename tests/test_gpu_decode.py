@@ -10,7 +10,8 @@ import torch
 import int8_mqa_kv_amd as mk
 import oracle
 import synth
-from tests.gpu_util import GpuCase, OracleKV, assert_parity, log, outlier_q, q_tensor
+from tests.gpu_util import (GpuCase, OracleKV, assert_parity, log, outlier_q, q_tensor,
+                            with_v_gain)
 
 pytestmark = pytest.mark.gpu
 
@@ -236,6 +237,15 @@ def test_outlier_query_channels(gain, window):
     out = g.decode(q)
     want = oracle.decode(q64, w.context_lens, w.layer_slot, w.layer_window, OracleKV(w))
     assert_parity(out.cpu().numpy(), want, f"outlier q x{gain}, window {window}")
+
+
+@pytest.mark.parametrize("window", [0, 1024], ids=["global", "window1024"])
+def test_v_scales_over_many_octaves(window):
+    """V rows that are zero, then 2^-80 of the usual size, then growing by
+    powers of two (see with_v_gain): the running V exponent starts absent,
+    is clamped, and moves many times within one wavefront's keys."""
+    _run_case(with_v_gain(synth.custom_decode(
+        62 + (window > 0), 5, 32, 128, "bf16", [45, 300, 1500, 4096, 9000], 1, window, 2000)))
 
 
 RAGGED_GLOBAL = {
