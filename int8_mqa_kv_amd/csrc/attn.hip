@@ -352,22 +352,27 @@ __device__ __forceinline__ void attend_block(WaveState<D, NRT>& st, const QOps<D
     st.ev = ev_new;
     st.ev_thr = ev_new == kNoExp ? 0.0f : ldexp2(1.0f, ev_new);
     float alpha[NRT];
-    bool rescale = false;
+    bool rescale = false, held = false;
 #pragma unroll
     for (int n = 0; n < NRT; ++n) {
       const float mt = row_max4(lmax[n]);
       const float mx = mt == kNegInf ? kNegInf : mt * q.crow[n];
       const bool move = mx > st.m[n] + kTau;  // also true for the first valid block
       const float m_new = move ? mx : st.m[n];
+      // a row whose reference is still -inf has seen no valid key: its sums
+      // are zero and need no rescale
+      const bool had = st.m[n] != kNegInf;
       alpha[n] = move ? fast_exp2(st.m[n] - m_new) : 1.0f;  // exp2(-inf) = 0
-      rescale |= move;
+      rescale |= move && had;
+      held |= had;
       st.off[n] = m_new == kNegInf ? (float)lpv : (float)lpv - m_new;
-      st.thr[n] = m_new == kNegInf ? kNegInf : (m_new + kTau) / q.crow[n];
+      st.thr[n] = m_new == kNegInf ? kNegInf : (m_new + kTau) * __builtin_amdgcn_rcpf(q.crow[n]);
       st.m[n] = m_new;
     }
-    // rescale only when some row's reference moved or the V exponent grew
-    // (wave-uniform branch)
-    if (__builtin_amdgcn_ballot_w64(rescale) != 0 || dexp != 0) {
+    // rescale only when a row with sums moved its reference, or the V
+    // exponent grew while some row had sums (wave-uniform branch)
+    if (__builtin_amdgcn_ballot_w64(rescale) != 0 ||
+        (dexp != 0 && __builtin_amdgcn_ballot_w64(held) != 0)) {
 #pragma unroll
       for (int n = 0; n < NRT; ++n) {
         const float f = ldexp2(alpha[n], dexp);
