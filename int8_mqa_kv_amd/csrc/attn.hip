@@ -203,10 +203,12 @@ __device__ __forceinline__ void convert_q(QOps<D, QS, NRT>& o, const QRaw<D, QS,
 // Lazy softmax reference: a row's reference max only moves when a block's max
 // exceeds it by more than kTau (log2 units), so p = exp2(sigma - m_ref) stays
 // below 2^kTau and most blocks skip rescaling the accumulators.  The weights
-// are formed already multiplied by 2^lpv, lpv = kPvBias - ev (ev: exponent of
-// the largest V scale seen; lpv = 0 while none was seen), through the
-// exponent's offset: P*sV then stays below 2^14 as an fp16 operand, and the
-// running sum l is kept in the same units until the key loop ends.  Both
+// are formed already multiplied by 2^lpv, lpv = kPvBias - ev, through the
+// exponent's offset (every V scale seen is below 2^ev; ev is set
+// kVExpHeadroom above the largest one's exponent whenever it moves, so that
+// later blocks rarely move it; lpv = 0 while no V scale was seen): P*sV then
+// stays below 2^14 as an fp16 operand, and the running sum l is kept in the
+// same units until the key loop ends.  Both
 // conditions are tested first against thresholds cached when the reference
 // last moved (a key's score times its scale, and a V scale, each compared in
 // its own lane); only a block that passes one works out row maxima across
@@ -215,6 +217,7 @@ __device__ __forceinline__ void convert_q(QOps<D, QS, NRT>& o, const QRaw<D, QS,
 // the full path and moves nothing; results stay deterministic.)
 constexpr float kTau = 8.0f;
 constexpr int kPvBias = 14 - 8;
+constexpr int kVExpHeadroom = 2;
 // Smallest V exponent tracked: keeps 2^lpv, and l in its units, finite for
 // absurdly small scales (a V scale below 2^-64 contributes below 2^-57 to any
 // output).
@@ -230,7 +233,8 @@ struct WaveState {
   float m[NRT];                // running max (log2 domain), equal on a row's 4 lanes
   float l[NRT];                // this lane's part of the row's running sum, in units of
                                // 2^lpv during the key loop (plain after finish())
-  int ev;                      // exponent of the largest V scale seen (kNoExp: none)
+  int ev;                      // every V scale seen is below 2^ev, set kVExpHeadroom above
+                               // the largest one's exponent when it moves (kNoExp: none)
   // Cached from the last time the reference or the V exponent moved: a key
   // scale times score above thr[n] moves row n's reference; a V scale at or
   // above ev_thr = 2^ev moves the exponent; off[n] = lpv - m (lpv for
@@ -345,7 +349,7 @@ __device__ __forceinline__ void attend_block(WaveState<D, NRT>& st, const QOps<D
     // Largest valid V scale of the block -> running exponent.
     const float vm = row_max4(vmax);
     int ev_new = st.ev;
-    if (vm > 0.0f) ev_new = max(ev_new, max(frexp_exp(vm), kMinVExp));
+    if (vm > 0.0f) ev_new = max(ev_new, max(frexp_exp(vm) + kVExpHeadroom, kMinVExp));
     const int lpv_old = st.ev == kNoExp ? 0 : kPvBias - st.ev;
     const int lpv = ev_new == kNoExp ? 0 : kPvBias - ev_new;
     const int dexp = lpv - lpv_old;  // the units of acc, psum and l change by 2^dexp
