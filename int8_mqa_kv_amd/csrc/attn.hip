@@ -256,21 +256,33 @@ struct WaveState {
     ev = kNoExp;
     ev_thr = 0.0f;
   }
-  // After the last key: the accumulators hold P.(V codes + kCodeBias), so
-  // kCodeBias * sum(P) comes out; l returns from units of 2^lpv.
-  __device__ __forceinline__ void finish() {
-    const float u = ev == kNoExp ? 1.0f : ldexp2(1.0f, ev - kPvBias);
+  // The accumulators hold P.(V codes + kCodeBias): take kCodeBias * sum(P)
+  // out and restart that sum.  Done every kRebiasBlocks blocks, not only at
+  // the end, so that the accumulators stay near the size of the result: the
+  // bias part grows with every block, and over a long key range its fp32
+  // rounding would otherwise outgrow an output that is an average over
+  // thousands of keys.
+  __device__ __forceinline__ void rebias() {
 #pragma unroll
     for (int n = 0; n < NRT; ++n) {
-      l[n] *= u;
 #pragma unroll
       for (int t = 0; t < Geo<D>::VT; ++t)
 #pragma unroll
         for (int k = 0; k < 4; ++k)
           acc[n][t][k] = __builtin_fmaf(-kCodeBias, psum[n][k], acc[n][t][k]);
+      psum[n] = f32x4{0, 0, 0, 0};
     }
   }
+  // After the last key: the remaining bias comes out; l returns from units
+  // of 2^lpv.
+  __device__ __forceinline__ void finish() {
+    rebias();
+    const float u = ev == kNoExp ? 1.0f : ldexp2(1.0f, ev - kPvBias);
+#pragma unroll
+    for (int n = 0; n < NRT; ++n) l[n] *= u;
+  }
 };
+constexpr int kRebiasBlocks = 32;
 
 // Attend the 32 keys of two consecutive logical pages.  pos0 is the position
 // of the first page's first token.  MASKED blocks (some key outside [lo, hi)
@@ -990,28 +1002,33 @@ __global__ __launch_bounds__(W * 64, 2) void decode_kernel(
 
   WaveState<D, NRT> st;
   st.init();
-  for (int b = 0; b < nblk; ++b) {
-    const int pa = pbeg + 2 * b;
-    const int cs = 2 * (b % RB);
-    // The compiler does not track global -> LDS loads: wait for them here.
-    // In flight are blocks b .. b+RB-2 (issued in order): leave the younger
-    // ones outstanding.
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((RB - 2) * DMA_PER_BLOCK));
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (NK != NewKV::kNone) {
-      if (b == b_cur)  // the one wavefront holding the current token (coded above)
-        cur.put(ring.ring[wv][cs + (p_last - pa)], tok, lane);
+  // in groups of kRebiasBlocks blocks, the code bias taken out between groups
+  for (int b0 = 0; b0 < nblk; b0 += kRebiasBlocks) {
+    const int b1 = min(b0 + kRebiasBlocks, nblk);
+    for (int b = b0; b < b1; ++b) {
+      const int pa = pbeg + 2 * b;
+      const int cs = 2 * (b % RB);
+      // The compiler does not track global -> LDS loads: wait for them here.
+      // In flight are blocks b .. b+RB-2 (issued in order): leave the younger
+      // ones outstanding.
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((RB - 2) * DMA_PER_BLOCK));
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (NK != NewKV::kNone) {
+        if (b == b_cur)  // the one wavefront holding the current token (coded above)
+          cur.put(ring.ring[wv][cs + (p_last - pa)], tok, lane);
+      }
+      PageRegs<D> c0, c1;
+      lds_page<D>(c0, ring.ring[wv][cs], lane, lg);
+      lds_page<D>(c1, ring.ring[wv][cs + 1], lane, lg);
+      int pid0, pid1;
+      const bool ok0 = page_ok(pa, pid0), ok1 = page_ok(pa + 1, pid1);
+      // block b+RB-1 into the slots read one iteration ago; flies during compute.
+      // With a 2-block ring every wait is vmcnt(0), so past the last block
+      // nothing needs issuing; deeper rings keep the per-block count constant.
+      if (RB > 2 || b + 1 < nblk) issue_block(pa + 2 * (RB - 1), 2 * ((b + RB - 1) % RB));
+      attend_block_any<D, QS, NRT>(st, q, c0, c1, ok0, ok1, pa * kPageTokens, lo, hi, lg);
     }
-    PageRegs<D> c0, c1;
-    lds_page<D>(c0, ring.ring[wv][cs], lane, lg);
-    lds_page<D>(c1, ring.ring[wv][cs + 1], lane, lg);
-    int pid0, pid1;
-    const bool ok0 = page_ok(pa, pid0), ok1 = page_ok(pa + 1, pid1);
-    // block b+RB-1 into the slots read one iteration ago; flies during compute.
-    // With a 2-block ring every wait is vmcnt(0), so past the last block
-    // nothing needs issuing; deeper rings keep the per-block count constant.
-    if (RB > 2 || b + 1 < nblk) issue_block(pa + 2 * (RB - 1), 2 * ((b + RB - 1) % RB));
-    attend_block_any<D, QS, NRT>(st, q, c0, c1, ok0, ok1, pa * kPageTokens, lo, hi, lg);
+    if (b1 < nblk) st.rebias();  // (the last group's bias comes out in finish())
   }
 
   st.finish();
@@ -1315,6 +1332,7 @@ __global__ __launch_bounds__(kAppendWaves * 64) void append_kernel(
   st.init();
   for (int b = 0; b < nblk; ++b) {
     const int rs = b % RB;
+    if (b % kRebiasBlocks == 0 && b > 0) st.rebias();  // the code bias out (wave-uniform)
     // this wavefront's pieces of block b have landed (blocks b+1 .. b+RB-2
     // may still be in flight) ...
     // (a page-id reload among the younger loads only makes this wait longer)

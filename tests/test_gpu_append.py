@@ -130,3 +130,13 @@ def test_append_v_scales_over_many_octaves():
     growing by powers of two (see with_v_gain)."""
     _run(with_v_gain(synth.custom_append(49, [20, 900, 3000], [30, 64, 17], 32, 128, [1024, 0],
                                          [0, 1])))
+
+
+@pytest.mark.parametrize("prefix", [16000, 32000])
+def test_append_long_global_prefix(prefix):
+    """A chunk over a long cached prefix on a global layer: every wavefront
+    walks the whole prefix in one workgroup (no split), so its accumulators
+    sum over 500-1000 blocks; the output, an average over that many keys, is
+    small, which makes the relative bound the tight one."""
+    w = synth.custom_append(50 + prefix // 16000, [prefix], [16], 32, 128, [0], [0])
+    _run(w)

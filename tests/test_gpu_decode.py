@@ -295,3 +295,16 @@ def test_many_sequences_split():
         _run_with_empty(w)
     finally:
         mk.decode_tuning()
+
+
+@pytest.mark.parametrize("target_wgs", [1, 8])
+def test_long_range_per_wavefront(target_wgs):
+    """One 32000-token global sequence split over very few workgroups, so each
+    wavefront walks 60-250 blocks: the accumulators' code bias is taken out
+    between groups of blocks, and the output, an average over 32000 keys,
+    stays within the relative bound."""
+    mk.decode_tuning(target_wgs=target_wgs)
+    try:
+        _run_case(synth.custom_decode(34, 1, 32, 128, "bf16", [32000], 1, 0, permuted_pool=2100))
+    finally:
+        mk.decode_tuning()
