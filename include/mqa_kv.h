@@ -56,6 +56,10 @@ extern "C" {
 
 #define MQA_KV_ABI_VERSION 5
 #define MQA_PAGE_TOKENS 16
+/* Largest max_context (tokens) that decode and append accept: 2^22 = 4,194,304.
+ * It keeps the kernels' page and chunk arithmetic within 32 bits; a larger
+ * bound is refused with MQA_ERR_UNSUPPORTED. */
+#define MQA_MAX_CONTEXT (1 << 22)
 
 typedef enum {
   MQA_OK = 0,
@@ -220,7 +224,7 @@ int mqa_decode_tuning(int32_t waves, int32_t rows, int32_t target_wgs);
  *                current one (which sits at position context_len-1).  Must
  *                lie in [1, max_context]; a length <= 0 gives zeros.
  *  max_context   (host) upper bound of context_lens, used to plan the launch
- *                without reading device memory.
+ *                without reading device memory; at most MQA_MAX_CONTEXT.
  *  layer_slot    (host) int32 [num_layers]: the KV slot each layer reads.
  *                Layers that read the same slot with the same window are
  *                served from one KV read (cross-layer KV sharing).

@@ -31,7 +31,7 @@ import numpy as np
 import torch  # noqa: F401  (import order matters, see above)
 
 __all__ = [
-    "PAGE_TOKENS", "MQAError", "KVPool", "lib", "page_bytes", "kv_bytes_per_token",
+    "PAGE_TOKENS", "MAX_CONTEXT", "MQAError", "KVPool", "lib", "page_bytes", "kv_bytes_per_token",
     "page_layout", "kv_pack_int8", "decode_workspace_bytes", "decode_workspace",
     "mqa_decode_attn", "mqa_decode_step", "mqa_decode_step_noalloc", "DECODE_STATIC_SCRATCH_BYTES",
     "mqa_append_attn", "slot_mapping_for", "unpack_page_tokens",
@@ -41,6 +41,7 @@ __all__ = [
 ]
 
 PAGE_TOKENS = 16
+MAX_CONTEXT = 1 << 22  # MQA_MAX_CONTEXT: the largest max_context decode and append accept
 _HERE = os.path.dirname(os.path.abspath(__file__))
 # MQA_KV_LIB selects another build of the library (the host-sanitizer build
 # of the CPU checks); by default the gfx950 build beside this file.

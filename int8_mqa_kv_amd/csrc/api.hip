@@ -82,6 +82,8 @@ int check_attn_common(const void* q, mqa_dtype q_dtype, const float* out, const 
   if (num_slots <= 0) return fail(MQA_ERR_INVALID, "num_slots must be > 0");
   if (max_pages_per_seq <= 0) return fail(MQA_ERR_INVALID, "max_pages_per_seq must be > 0");
   if (max_context <= 0) return fail(MQA_ERR_INVALID, "max_context must be > 0");
+  if (max_context > MQA_MAX_CONTEXT)
+    return fail(MQA_ERR_UNSUPPORTED, "max_context %d above %d", max_context, MQA_MAX_CONTEXT);
   if ((int64_t)max_pages_per_seq * kPageTokens < max_context)
     return fail(MQA_ERR_INVALID, "max_pages_per_seq*16 = %lld < max_context %d",
                 (long long)max_pages_per_seq * kPageTokens, max_context);
@@ -228,6 +230,8 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
     items += n;
     work += n * max_np[g];
   }
+  static_assert((MQA_MAX_CONTEXT / kPageTokens + 1 + 255) / 256 <= kMaxDecodeChunks,
+                "every wavefront's pages fit one register of page ids at the largest context");
   // Chunks per item: a share of the target workgroup count in proportion to
   // the item's span, so that one round of workgroups covers the launch with
   // equal work per workgroup and none left idle; at least enough chunks that
@@ -237,7 +241,8 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
   for (size_t g = 0; g < keys.size(); ++g) {
     const int64_t share = target * max_np[g] / std::max<int64_t>(work, 1);
     const int64_t need = (max_np[g] + 64 * waves - 1) / (64 * waves);
-    nchunk[g] = std::max<int64_t>({1, share, need});
+    // at most kMaxDecodeChunks (under MQA_MAX_CONTEXT, need stays below it)
+    nchunk[g] = std::min<int64_t>(std::max<int64_t>({1, share, need}), kMaxDecodeChunks);
   }
 
   int rb = 0;
@@ -390,7 +395,8 @@ int kv_pack_int8(const void* k, const void* v, mqa_dtype src_dtype, int64_t num_
 size_t mqa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_layers,
                                   const int32_t* layer_slot, const int32_t* layer_window,
                                   int32_t max_context, int32_t head_dim, mqa_dtype q_dtype) {
-  if (batch <= 0 || num_q_heads <= 0 || num_layers <= 0 || max_context <= 0 || !layer_slot ||
+  if (batch <= 0 || num_q_heads <= 0 || num_layers <= 0 || max_context <= 0 ||
+      max_context > MQA_MAX_CONTEXT || !layer_slot ||
       !layer_window || (head_dim != 64 && head_dim != 128) ||
       (q_dtype != MQA_F32 && q_dtype != MQA_BF16))
     return 0;

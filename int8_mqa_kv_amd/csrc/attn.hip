@@ -491,7 +491,8 @@ struct WaveSpan {
     const int p_first = lo >> 4;
     p_last = (hi - 1) >> 4;
     const int np = p_last - p_first + 1;
-    // (np <= 2^20 pages and chunks < 2^11 keep the products in 32 bits)
+    // (the host bounds max_context by 2^22 keys and the chunks by 2^11:
+    // np <= 2^18 + 1 pages, so the products stay within 32 bits)
     const int npb = window > 0 ? np : max((ctx_cap + kPageTokens - 1) / kPageTokens, 1);
     const int nchb = min(nchunk, max(1, (npb + 2 * W - 1) / (2 * W)));
     nch = window > 0 ? nchb : (int)(((uint32_t)(np * nchb) + npb - 1) / (uint32_t)npb);

@@ -144,5 +144,6 @@ constexpr int64_t kCounterWords = kDecodeCounters * kCounterStride;  // 8 MiB pr
 constexpr int kDecodeWaves = 8;     // wavefronts per decode workgroup (one workgroup per CU)
 constexpr int kDecodeWavesSmall = 4;  // the two-per-CU shape for launches with few items
 constexpr int kDecodeRing = 2;      // blocks of two pages in flight per wavefront
+constexpr int kMaxDecodeChunks = 2048;  // chunks of one item's key range, at most
 
 }  // namespace mqa

@@ -96,6 +96,8 @@ def _call_decode(**kw):
     (dict(q=0x1002), mk.MQA_ERR_INVALID, "aligned"),
     (dict(layer_window=[0], max_context=32768, max_pages=2048, batch=16),
      mk.MQA_ERR_WORKSPACE, "workspace"),
+    (dict(max_context=mk.MAX_CONTEXT + 1, max_pages=mk.MAX_CONTEXT // 16 + 1),
+     mk.MQA_ERR_UNSUPPORTED, "max_context"),
 ])
 def test_decode_rejects_bad_arguments(kw, code, text):
     rc, msg = _call_decode(**kw)
@@ -118,6 +120,24 @@ def test_decode_workspace_sizes():
     with pytest.raises(ValueError):
         mk.decode_workspace_bytes(16, 32, [0], [0], 32768, 128, 'f16')
     assert ws1 >= 0
+
+
+def test_decode_context_bound():
+    """max_context is accepted up to MQA_MAX_CONTEXT (2^22 tokens), where the
+    kernels' page and chunk arithmetic still fits 32 bits, and refused above.
+    The chunk count per item is capped at 2048 even when the workgroup target
+    asks for more, which keeps the per-chunk page ranges in the same range."""
+    assert mk.MAX_CONTEXT == 1 << 22
+    at = mk.decode_workspace_bytes(1, 32, [0], [0], mk.MAX_CONTEXT, 128)
+    assert at > 0
+    assert mk.decode_workspace_bytes(1, 32, [0], [0], mk.MAX_CONTEXT + 1, 128) == 0
+    rec = 16 * 288 * 4  # one partial record: 16 (row tile, channel tile) pairs x 288 fp32
+    mk.decode_tuning(target_wgs=1 << 20)
+    try:
+        assert mk.decode_workspace_bytes(1, 32, [0], [0], mk.MAX_CONTEXT, 128) == (8 << 20) + 2048 * rec
+    finally:
+        mk.decode_tuning()
+    assert mk.decode_workspace_bytes(1, 32, [0], [0], mk.MAX_CONTEXT, 128) == at
 
 
 def _ws_with_waves(args, waves):
@@ -172,6 +192,11 @@ def test_append_rejects_bad_arguments():
                                 0x4000, None, 1024, 64, 64, 1, 32, 1, 1, ls.ctypes.data,
                                 lw.ctypes.data, 0.0, None)
     assert rc == mk.MQA_ERR_INVALID and "cu_q_lens" in mk.lib.mqa_last_error().decode()
+    big = mk.MAX_CONTEXT + 1
+    rc = mk.lib.mqa_append_attn(0x1000, mk.MQA_BF16, 0x2000, ctypes.byref(_pool()), 0x3000,
+                                big // 16 + 1, 0x4000, 0x5000, big, 64, 64, 1, 32, 1, 1,
+                                ls.ctypes.data, lw.ctypes.data, 0.0, None)
+    assert rc == mk.MQA_ERR_UNSUPPORTED and "max_context" in mk.lib.mqa_last_error().decode()
 
 
 def test_unpack_roundtrip_on_host():

@@ -297,6 +297,32 @@ def test_many_sequences_split():
         mk.decode_tuning()
 
 
+@pytest.mark.timeout(600)
+def test_decode_at_the_context_bound():
+    """One sequence of MQA_MAX_CONTEXT (2^22) tokens, the largest context the
+    library accepts, on a permuted pool of 262,241 pages.  The planner's own
+    plan splits it into about 500 chunks; a workgroup target of 2^20 forces
+    the 2048-chunk cap.  Either way the chunks' page ranges, worked out in
+    32-bit arithmetic in the kernel, must tile the 262,144 pages, and the last
+    arrival folds every chunk's record.  Both plans are checked against one
+    oracle result."""
+    w = synth.custom_decode(35, 1, 8, 64, "bf16", [mk.MAX_CONTEXT], 1, 0,
+                            permuted_pool=mk.MAX_CONTEXT // 16 + 97)
+    log(f"decode at the context bound: ctx {mk.MAX_CONTEXT}, Hq=8, d=64")
+    g = GpuCase(w)
+    q, q64 = q_tensor(w)
+    want = oracle.decode(q64, w.context_lens, w.layer_slot, w.layer_window, OracleKV(w))
+    for target in (0, 1 << 20):
+        mk.decode_tuning(target_wgs=target)
+        try:
+            log(f"  workgroup target {target or 'planner'}: workspace "
+                f"{mk.decode_workspace_bytes(1, 8, [0], [0], mk.MAX_CONTEXT, 64)} bytes")
+            out = g.decode(q)
+        finally:
+            mk.decode_tuning()
+        assert_parity(out.cpu().numpy(), want, f"context bound, target {target}")
+
+
 @pytest.mark.parametrize("target_wgs", [1, 8])
 def test_long_range_per_wavefront(target_wgs):
     """One 32000-token global sequence split over very few workgroups, so each
