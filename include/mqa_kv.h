@@ -473,7 +473,8 @@ int mqa_page_table_slot_mapping(const mqa_page_table* table, int32_t seq, int32_
  *          (negative or past the pool: skipped).
  * decode:  q bf16 [batch][num_q_heads][head_dim]; out fp32 same shape;
  *          block_table int32 [batch][max_pages]; context_lens int32 [batch]
- *          (the query at context-1); window 0 = global.  Contexts split over
+ *          (the query at context-1); max_context at most MQA_MAX_CONTEXT;
+ *          window 0 = global.  Contexts split over
  *          workgroups use `workspace` (mqa_gqa_decode_workspace_bytes(),
  *          no clearing needed) and a second small kernel merges them.
  * Errors as for the other entry points.

@@ -350,6 +350,9 @@ int gqa_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t m
     return fail(MQA_ERR_UNSUPPORTED, "more than %d query heads per KV head", kGqaMaxGroup);
   if (head_dim != 64 && head_dim != 128) return fail(MQA_ERR_UNSUPPORTED, "head_dim %d", head_dim);
   if (max_context < 0 || window < 0) return fail(MQA_ERR_INVALID, "negative context or window");
+  // (bounded so that the kernel's 32-bit chunk boundaries cannot wrap)
+  if (max_context > MQA_MAX_CONTEXT)
+    return fail(MQA_ERR_UNSUPPORTED, "max_context %d above %d", max_context, MQA_MAX_CONTEXT);
   const int64_t ctx_pages = (max_context + 15) / 16;
   const int64_t max_np = window > 0 ? std::min<int64_t>((window + 15) / 16 + 1, ctx_pages) : ctx_pages;
   const int64_t items = (int64_t)batch * num_kv_heads;

@@ -140,6 +140,14 @@ def test_decode_context_bound():
     assert mk.decode_workspace_bytes(1, 32, [0], [0], mk.MAX_CONTEXT, 128) == at
 
 
+def test_gqa_context_bound():
+    """The grouped-query baseline takes the same bound on max_context."""
+    at = mk.lib.mqa_gqa_decode_workspace_bytes(1, 32, 8, mk.MAX_CONTEXT, 0, 128)
+    assert at > 0
+    assert mk.lib.mqa_gqa_decode_workspace_bytes(1, 32, 8, mk.MAX_CONTEXT + 1, 0, 128) == 0
+    assert "max_context" in mk.lib.mqa_last_error().decode()
+
+
 def _ws_with_waves(args, waves):
     mk.decode_tuning(waves=waves)
     try:
