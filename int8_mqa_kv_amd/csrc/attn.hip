@@ -463,7 +463,7 @@ __device__ __forceinline__ void attend_block_any(WaveState<D, NRT>& st, const QO
 }
 
 __device__ __forceinline__ int clamp_ctx(int ctx, int max_context, int max_pages) {
-  const int cap = min(max_context, max_pages * kPageTokens);
+  const int cap = (int)min<int64_t>(max_context, (int64_t)max_pages * kPageTokens);
   return min(max(ctx, 0), cap);
 }
 

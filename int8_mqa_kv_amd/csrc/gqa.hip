@@ -121,7 +121,7 @@ __global__ __launch_bounds__(kGqaWaves * 64) void gqa_decode_kernel(
     if (li < G) x = *reinterpret_cast<const u32x4*>(q + (qrow0 + li) * D + 32 * s + 8 * lg);
     qop[s] = __builtin_bit_cast(bf16x8, x);
   }
-  const int cap = min(a.max_context, a.max_pages * 16);
+  const int cap = (int)min<int64_t>(a.max_context, (int64_t)a.max_pages * 16);
   const int ctx = min(max(context_lens[seq], 0), cap);
   const int hi = ctx, lo = a.window > 0 ? max(0, ctx - a.window) : 0;
   const int p_first = lo >> 4, p_last = hi > lo ? (hi - 1) >> 4 : p_first - 1;
@@ -309,7 +309,7 @@ __global__ __launch_bounds__(256) void gqa_merge_kernel(const GqaArgs a, float* 
                                                         const float* __restrict__ ws) {
   const int it = blockIdx.x;
   const int seq = it / a.num_kv_heads, head = it % a.num_kv_heads;
-  const int cap = min(a.max_context, a.max_pages * 16);
+  const int cap = (int)min<int64_t>(a.max_context, (int64_t)a.max_pages * 16);
   const int ctx = min(max(context_lens[seq], 0), cap);
   const int lo = a.window > 0 ? max(0, ctx - a.window) : 0;
   if (ctx <= lo) return;  // the decode kernel wrote zeros
