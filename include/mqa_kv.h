@@ -60,6 +60,11 @@ extern "C" {
  * It keeps the kernels' page and chunk arithmetic within 32 bits; a larger
  * bound is refused with MQA_ERR_UNSUPPORTED. */
 #define MQA_MAX_CONTEXT (1 << 22)
+/* Largest number of tokens one kv_pack_int8 call takes (of (token, KV head)
+ * pairs for mqa_gqa_pack_bf16): 2^25, which keeps the launch within the
+ * work-items one dispatch can hold.  Larger inputs are packed in several
+ * calls; a larger count is refused with MQA_ERR_UNSUPPORTED. */
+#define MQA_PACK_MAX_TOKENS (1 << 25)
 
 typedef enum {
   MQA_OK = 0,
@@ -140,6 +145,7 @@ int mqa_page_offset(int32_t head_dim, int32_t token, int32_t channel,
  *
  *  k, v          [num_tokens rows] of head_dim values of `src_dtype`; row t
  *                starts at element t*row_stride (row_stride >= head_dim).
+ *                num_tokens is at most MQA_PACK_MAX_TOKENS per call.
  *  slot_mapping  int64 [num_tokens]: page*16 + offset_in_page of each token;
  *                a negative entry skips that token (padding).
  *  pool          (host) the page pool written.
@@ -468,7 +474,8 @@ int mqa_page_table_slot_mapping(const mqa_page_table* table, int32_t seq, int32_
  * 64*head_dim bytes at h*64*head_dim, its 16 tokens' K then V in bf16
  * matrix-core operand order (the order mqa_gqa_pack_bf16 writes).
  *
- * pack:    k, v (device) bf16 [num_tokens][num_kv_heads][head_dim];
+ * pack:    k, v (device) bf16 [num_tokens][num_kv_heads][head_dim], with
+ *          num_tokens*num_kv_heads at most MQA_PACK_MAX_TOKENS per call;
  *          slot_mapping int64 [num_tokens] = page*16 + position in page
  *          (negative or past the pool: skipped).
  * decode:  q bf16 [batch][num_q_heads][head_dim]; out fp32 same shape;

@@ -376,7 +376,9 @@ int kv_pack_int8(const void* k, const void* v, mqa_dtype src_dtype, int64_t num_
   if (src_dtype != MQA_F32 && src_dtype != MQA_BF16)
     return fail(MQA_ERR_UNSUPPORTED, "source dtype %d unsupported", (int)src_dtype);
   if (num_tokens < 0) return fail(MQA_ERR_INVALID, "num_tokens is negative");
-  if (num_tokens > (INT64_C(1) << 33)) return fail(MQA_ERR_INVALID, "num_tokens too large");
+  if (num_tokens > MQA_PACK_MAX_TOKENS)
+    return fail(MQA_ERR_UNSUPPORTED, "num_tokens %lld above %d per call", (long long)num_tokens,
+                MQA_PACK_MAX_TOKENS);
   if (num_tokens == 0) return ok();
   if (row_stride < pool->head_dim)
     return fail(MQA_ERR_INVALID, "row_stride %lld < head_dim %d", (long long)row_stride,

@@ -388,6 +388,9 @@ int mqa_gqa_pack_bf16(const void* k, const void* v, int64_t num_tokens, const in
   if (num_tokens < 0) return fail(MQA_ERR_INVALID, "num_tokens < 0");
   if (num_kv_heads < 1) return fail(MQA_ERR_INVALID, "num_kv_heads < 1");
   if (head_dim != 64 && head_dim != 128) return fail(MQA_ERR_UNSUPPORTED, "head_dim %d", head_dim);
+  if (num_tokens * num_kv_heads > MQA_PACK_MAX_TOKENS)
+    return fail(MQA_ERR_UNSUPPORTED, "%lld (token, KV head) pairs above %d per call",
+                (long long)num_tokens * num_kv_heads, MQA_PACK_MAX_TOKENS);
   if (num_tokens == 0) return ok();
   if (!k || !v || !slot_mapping || !pool) return fail(MQA_ERR_INVALID, "NULL pointer");
   if (num_pages <= 0 || !aligned256(pool)) return fail(MQA_ERR_INVALID, "bad pool");

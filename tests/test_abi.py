@@ -191,6 +191,13 @@ def test_pack_rejects_bad_arguments():
     assert rc == mk.MQA_ERR_INVALID and "row_stride" in mk.lib.mqa_last_error().decode()
     rc = mk.lib.kv_pack_int8(0x1000, 0x2000, mk.MQA_F32, 0, 128, 0x3000, ctypes.byref(_pool()), None)
     assert rc == mk.MQA_OK
+    # one call packs at most MQA_PACK_MAX_TOKENS = 2^25 tokens (a launch holds 2^32 - 1
+    # work-items, 64 per token)
+    rc = mk.lib.kv_pack_int8(0x1000, 0x2000, mk.MQA_F32, (1 << 25) + 1, 128, 0x3000,
+                             ctypes.byref(_pool()), None)
+    assert rc == mk.MQA_ERR_UNSUPPORTED and "per call" in mk.lib.mqa_last_error().decode()
+    rc = mk.lib.mqa_gqa_pack_bf16(0x1000, 0x2000, (1 << 22) + 1, 0x3000, 0x4000, 10, 8, 128, None)
+    assert rc == mk.MQA_ERR_UNSUPPORTED and "per call" in mk.lib.mqa_last_error().decode()
 
 
 def test_append_rejects_bad_arguments():
