@@ -276,8 +276,9 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
     ws += (int64_t)G.num_rb * batch * G.nchunk;
     merges += (int64_t)G.num_rb * batch;
   }
-  if (wg > (INT64_C(1) << 30) || ws > (INT64_C(1) << 30)) {
-    p.rc = fail(MQA_ERR_UNSUPPORTED, "launch too large");
+  // one dispatch holds at most 2^32 - 1 work-items (the grid is padded to a multiple of 8)
+  if ((wg + 8) * waves * 64 > INT64_C(0xFFFFFFFF) || ws > (INT64_C(1) << 30)) {
+    p.rc = fail(MQA_ERR_UNSUPPORTED, "launch too large: %lld workgroups", (long long)wg);
     return p;
   }
   a.num_groups = (int)keys.size();
@@ -538,7 +539,9 @@ int mqa_append_attn(const void* q, mqa_dtype q_dtype, float* out, const mqa_kv_p
   const int head_blocks = (num_q_heads + kRowsPerBlock - 1) / kRowsPerBlock;
   const int token_blocks = (max_q_len + kAppendWaves - 1) / kAppendWaves;
   const int64_t total = (int64_t)num_layers * batch * head_blocks * token_blocks;
-  if (total > (INT64_C(1) << 31) - 8) return fail(MQA_ERR_UNSUPPORTED, "launch too large");
+  // one dispatch holds at most 2^32 - 1 work-items (the grid is padded to a multiple of 8)
+  if ((total + 8) * kAppendWaves * 64 > INT64_C(0xFFFFFFFF))
+    return fail(MQA_ERR_UNSUPPORTED, "launch too large: %lld workgroups", (long long)total);
   // layers ordered by slot, so layers sharing a slot run back to back
   std::vector<int> order(num_layers);
   for (int l = 0; l < num_layers; ++l) order[l] = l;
