@@ -359,7 +359,9 @@ int gqa_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t m
   const int64_t target = std::max<int64_t>(256, items);
   const int64_t need = (max_np + 64 * kGqaWaves - 1) / (64 * kGqaWaves);
   const int64_t nchunk = std::max<int64_t>({1, target / std::max<int64_t>(items, 1), need});
-  if (items * nchunk > (INT64_C(1) << 30)) return fail(MQA_ERR_UNSUPPORTED, "launch too large");
+  // one dispatch holds at most 2^32 - 1 work-items
+  if (items * nchunk * kGqaWaves * 64 > INT64_C(0xFFFFFFFF))
+    return fail(MQA_ERR_UNSUPPORTED, "launch too large: %lld workgroups", (long long)(items * nchunk));
   a.batch = batch;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;

@@ -148,6 +148,9 @@ def test_gqa_context_bound():
     assert at > 0
     assert mk.lib.mqa_gqa_decode_workspace_bytes(1, 32, 8, mk.MAX_CONTEXT + 1, 0, 128) == 0
     assert "max_context" in mk.lib.mqa_last_error().decode()
+    # 2^21 sequences x 8 KV heads: 2^24 workgroups of 512 work-items, past one dispatch
+    assert mk.lib.mqa_gqa_decode_workspace_bytes(1 << 21, 32, 8, 1024, 0, 128) == 0
+    assert "launch too large" in mk.lib.mqa_last_error().decode()
 
 
 def _ws_with_waves(args, waves):
