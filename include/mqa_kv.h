@@ -236,7 +236,8 @@ int mqa_decode_tuning(int32_t waves, int32_t rows, int32_t target_wgs);
  *                served from one KV read (cross-layer KV sharing).
  *  layer_window  (host) int32 [num_layers]: 0 = global, W > 0 = the last W
  *                positions (the query's own included).
- *  softmax_scale <= 0 selects 1/sqrt(head_dim).
+ *  softmax_scale <= 0 selects 1/sqrt(head_dim); NaN, an infinity or a scale
+ *                whose product with log2(e) overflows fp32 is refused.
  *  workspace     at least mqa_decode_workspace_bytes(...) bytes, 256-byte
  *                aligned, zero-filled before its first use (see above).  May
  *                be NULL when that size is 0.  Calls sharing one workspace

@@ -105,6 +105,13 @@ int check_attn_common(const void* q, mqa_dtype q_dtype, const float* out, const 
   return MQA_OK;
 }
 
+// A softmax scale the kernels can use: <= 0 (the default), or positive with
+// scale * log2(e) finite in fp32.  NaN and infinities are refused.
+bool scale_ok(float softmax_scale) {
+  return softmax_scale <= 0.0f ||
+         (softmax_scale > 0.0f && (double)softmax_scale * 1.4426950408889634 <= 3.4028234663852886e38);
+}
+
 float scale_log2_of(float softmax_scale, int head_dim) {
   const double s = softmax_scale > 0.0f ? (double)softmax_scale : 1.0 / sqrt((double)head_dim);
   return (float)(s * 1.4426950408889634);
@@ -446,6 +453,8 @@ int decode_common(const void* q, mqa_dtype q_dtype, float* out, const void* k_ne
                              max_context, batch, num_q_heads, num_layers, num_slots, layer_slot,
                              layer_window);
   if (rc) return rc;
+  if (!scale_ok(softmax_scale))
+    return fail(MQA_ERR_INVALID, "softmax_scale %g is not a usable number", (double)softmax_scale);
   DecodePlan p = plan_decode_auto(batch, num_q_heads, num_layers, layer_slot, layer_window,
                                   max_context, pool->head_dim, q_dtype == MQA_F32);
   if (p.rc) return p.rc;
@@ -531,6 +540,8 @@ int mqa_append_attn(const void* q, mqa_dtype q_dtype, float* out, const mqa_kv_p
   if (!cu_q_lens) return fail(MQA_ERR_INVALID, "cu_q_lens must be non-NULL");
   if (max_q_len <= 0) return fail(MQA_ERR_INVALID, "max_q_len must be > 0");
   if (total_q <= 0) return fail(MQA_ERR_INVALID, "total_q must be > 0");
+  if (!scale_ok(softmax_scale))
+    return fail(MQA_ERR_INVALID, "softmax_scale %g is not a usable number", (double)softmax_scale);
   if (num_layers > kMaxLayers)
     return fail(MQA_ERR_UNSUPPORTED, "%d layers in one append call; at most %d", num_layers,
                 kMaxLayers);

@@ -439,7 +439,9 @@ int mqa_gqa_decode_bf16(const void* q, float* out, const void* pool, int64_t num
     return fail(MQA_ERR_INVALID, "q and out must be 16-byte aligned");
   if (ws && (!workspace || workspace_bytes < ws))
     return fail(MQA_ERR_WORKSPACE, "workspace of %zu bytes needed", ws);
-  if (!(softmax_scale >= 0.0f)) return fail(MQA_ERR_INVALID, "softmax_scale must be >= 0");
+  if (!(softmax_scale >= 0.0f) ||
+      (double)softmax_scale * 1.4426950408889634 > 3.4028234663852886e38)
+    return fail(MQA_ERR_INVALID, "softmax_scale must be >= 0 and finite (scale * log2(e) in fp32)");
   const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf((float)head_dim);
   a.num_pages = num_pages;
   a.max_pages = max_pages;

@@ -100,6 +100,9 @@ def _call_decode(**kw):
      mk.MQA_ERR_UNSUPPORTED, "max_context"),
     (dict(batch=1 << 24, max_pages=64, max_context=1024), mk.MQA_ERR_UNSUPPORTED,
      "launch too large"),
+    (dict(scale=float("nan")), mk.MQA_ERR_INVALID, "softmax_scale"),
+    (dict(scale=float("inf")), mk.MQA_ERR_INVALID, "softmax_scale"),
+    (dict(scale=3e38), mk.MQA_ERR_INVALID, "softmax_scale"),
 ])
 def test_decode_rejects_bad_arguments(kw, code, text):
     rc, msg = _call_decode(**kw)
@@ -218,6 +221,10 @@ def test_append_rejects_bad_arguments():
                                 0x4000, cu, 1024, 1024, 1 << 30, 1 << 20, 32, 1, 1,
                                 ls.ctypes.data, lw.ctypes.data, 0.0, None)
     assert rc == mk.MQA_ERR_UNSUPPORTED and "launch too large" in mk.lib.mqa_last_error().decode()
+    rc = mk.lib.mqa_append_attn(0x1000, mk.MQA_BF16, 0x2000, ctypes.byref(_pool()), 0x3000, 64,
+                                0x4000, 0x5000, 1024, 64, 64, 1, 32, 1, 1, ls.ctypes.data,
+                                lw.ctypes.data, float("nan"), None)
+    assert rc == mk.MQA_ERR_INVALID and "softmax_scale" in mk.lib.mqa_last_error().decode()
     big = mk.MAX_CONTEXT + 1
     rc = mk.lib.mqa_append_attn(0x1000, mk.MQA_BF16, 0x2000, ctypes.byref(_pool()), 0x3000,
                                 big // 16 + 1, 0x4000, 0x5000, big, 64, 64, 1, 32, 1, 1,
