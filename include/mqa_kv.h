@@ -305,6 +305,10 @@ int mqa_decode_step(const void* q, mqa_dtype q_dtype, float* out,
  *  cu_q_lens     int32 [batch+1]: prefix sums of the chunk lengths
  *                (cu_q_lens[0] = 0, cu_q_lens[batch] = total_q).
  *  max_q_len     (host) upper bound of the chunk lengths.
+ * Device-side lengths that break these rules are not errors the host can
+ * see: rows of a chunk past max_q_len, and every row of a sequence whose rows
+ * fall outside [0, total_q), are left unwritten; nothing is read or written
+ * out of bounds.
  * Other arguments as for mqa_decode_attn.  No workspace is needed.
  */
 int mqa_append_attn(const void* q, mqa_dtype q_dtype, float* out,
