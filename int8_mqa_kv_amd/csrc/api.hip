@@ -288,6 +288,13 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_layers,
     p.rc = fail(MQA_ERR_UNSUPPORTED, "launch too large: %lld workgroups", (long long)wg);
     return p;
   }
+  // a slot whose pages exactly one row block reads: nothing reuses them
+  for (size_t g = 0; g < keys.size(); ++g) {
+    int readers = 0;
+    for (size_t h = 0; h < keys.size(); ++h)
+      if (keys[h].first == keys[g].first) readers += a.groups[h].num_rb;
+    a.groups[g].stream_once = readers == 1;
+  }
   a.num_groups = (int)keys.size();
   a.total_wgs = (int)wg;
   a.total_merge = (int)merges;
