@@ -578,6 +578,7 @@ __device__ __forceinline__ DecodeWork decode_work(const DecodeArgs& a, int w) {
   d.g.ws_begin = vg.ws_begin;
   d.g.merge_begin = vg.merge_begin;
   d.g.writes_new_kv = vg.writes_new_kv;
+  d.g.nontemporal = vg.nontemporal;
   d.g.rb_recip = vg.rb_recip;
   d.g.ch_recip = vg.ch_recip;
   udiv_recip((uint32_t)(w - d.g.wg_begin), (uint32_t)d.g.num_rb, d.g.rb_recip, q, r);
@@ -978,19 +979,17 @@ __global__ __launch_bounds__(W * 64, 2) void decode_kernel(
     }
   }
   // branch-free: a page that is out of range or has a bad id loads page 0
-  // instead (it exists) and is masked later.  Pages that only this row block
-  // reads go through the caches non-temporally: nothing reuses them, and
-  // keeping them out of the caches' retention measured 7 % faster where every
-  // page is read once; pages the row blocks of several layers or head blocks
-  // share keep the normal policy, since those readers hit the L2.
-  const bool stream_once = g.stream_once != 0;  // uniform
+  // instead (it exists) and is masked later.  Where the planner finds that
+  // nothing reuses the pages soon (one reader, or readers that reach each page
+  // close together), they go through the caches non-temporally.
+  const bool nontemporal = g.nontemporal != 0;  // uniform
   auto issue_block = [&](int pa, int slot0) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       int pid;
       const bool ok = page_ok(pa + u, pid);
       const uint8_t* rec = pool + (int64_t)(ok ? pid : 0) * page_bytes(D);
-      if (stream_once)
+      if (nontemporal)
         dma_page<D, kCpolNonTemporal>(ring.ring[wv][slot0 + u], rec, lane);
       else
         dma_page<D>(ring.ring[wv][slot0 + u], rec, lane);

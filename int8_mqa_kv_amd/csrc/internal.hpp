@@ -34,7 +34,7 @@ struct DecodeGroup {
   int32_t ws_begin;        // first workspace record of the group
   int32_t merge_begin;     // first arrival counter of the group (row blocks x batch before it)
   int32_t writes_new_kv;   // this group stores the slot's current token (first group of a slot)
-  int32_t stream_once;     // no other row block of the launch reads this slot's pages
+  int32_t nontemporal;     // page loads bypass the caches' retention (nothing reuses them soon)
   uint32_t rb_recip;       // floor((2^32 - 1) / num_rb): division by num_rb (udiv_recip)
   uint32_t ch_recip;       // floor((2^32 - 1) / nchunk)
 };
