@@ -146,9 +146,12 @@ __global__ __launch_bounds__(kGqaWaves * 64) void gqa_decode_kernel(
       const bool ok = page_ok(pa + u, pid);
       const uint8_t* src = pool + (ok ? (int64_t)pid : 0) * page_stride + head_off + lane * 16;
       uint8_t* dst = &sm.slot[wv][u][0];
+      // each workgroup reads only its KV head's part of a page, so nothing
+      // reuses these bytes: non-temporal (the cache-policy operand's nt bit),
+      // as the multi-query decode does for pages with one reader
 #pragma unroll
       for (int piece = 0; piece < HP / 1024; ++piece)
-        __builtin_amdgcn_global_load_lds(src + piece * 1024, dst + piece * 1024, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(src + piece * 1024, dst + piece * 1024, 16, 0, 2);
     }
   };
   const int nblk = (pend - pbeg + 1) >> 1;
