@@ -607,7 +607,7 @@ constexpr int lds_slot_bytes() { return page_bytes(D) + 128; }
 // both the global and the LDS address, so every piece of a page shares one
 // address computation and one LDS base.
 // Cache policy of a page load: 0, or the non-temporal bit for pages that
-// nothing else in the launch reads.
+// nothing reuses soon (the planner's choice per group).
 constexpr int kCpolNonTemporal = 2;
 
 template <int OFF, int CPOL>
